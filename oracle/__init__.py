@@ -1,0 +1,158 @@
+"""CPU oracle for tree-masked verification (test infrastructure only).
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this package.  It wraps the plain C oracle in `svt_oracle.c` with
+numpy-friendly functions; it never touches the GPU library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "svt_oracle.c")
+_LIB = os.path.join(_HERE, "libsvt_oracle.so")
+
+OK, ERR_ARG, ERR_TREE_ROOT, ERR_TREE_RANGE, ERR_TREE_CYCLE, ERR_CAPACITY, ERR_LENGTH = 0, -1, -3, -4, -5, -6, -9
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (ISO C11: no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                               _SRC, "-lm", "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_validate.argtypes = [P, i32, i32, P]
+        L.oracle_validate.restype = ctypes.c_int
+        L.oracle_mask.argtypes = [P, i32, i32, P, P, P]
+        L.oracle_mask.restype = None
+        L.oracle_attention.argtypes = [P, P, P, P, P, P, P, i32, i64, P, i32, i32, i32, i32, i32, dbl, P]
+        L.oracle_attention.restype = ctypes.c_int
+        L.oracle_attention_row.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, dbl, P]
+        L.oracle_attention_row.restype = None
+        L.oracle_argmax.argtypes = [P, i64, i32, P]
+        L.oracle_argmax.restype = None
+        L.oracle_accept.argtypes = [P, P, P, P, i32, i32, P, P, P]
+        L.oracle_accept.restype = None
+        L.oracle_commit.argtypes = [P, P, i32, i32, i32, i64, i32, i32, P, P, P, P, P, P, P, P]
+        L.oracle_commit.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def validate(parents: np.ndarray, M: int):
+    par = _c(parents, np.int32).reshape(-1, M + 1)
+    st = np.zeros(par.shape[0], dtype=np.int32)
+    first = lib().oracle_validate(_p(par), par.shape[0], M, _p(st))
+    return first, st
+
+
+def mask(parents: np.ndarray, M: int, status=None):
+    par = _c(parents, np.int32).reshape(-1, M + 1)
+    B, T = par.shape
+    W = (T + 63) // 64
+    mk = np.zeros((B, T, W), dtype=np.uint64)
+    dp = np.zeros((B, T), dtype=np.int32)
+    st = None if status is None else _c(status, np.int32)
+    lib().oracle_mask(_p(par), B, M, _p(st), _p(mk), _p(dp))
+    return mk, dp
+
+
+def attention(q, k_cache, v_cache, k_tree, v_tree, mk, lens, lmax: int, status=None,
+              scale: float | None = None):
+    """All tensor inputs float32 (exact upcasts).  Returns (rc, out float64)."""
+    q = _c(q, np.float32)
+    B, T, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    kc, vc = _c(k_cache, np.float32), _c(v_cache, np.float32)
+    kt, vt = _c(k_tree, np.float32), _c(v_tree, np.float32)
+    mk = _c(mk, np.uint64)
+    ln = _c(lens, np.int32)
+    st = None if status is None else _c(status, np.int32)
+    out = np.zeros((B, T, Hq, D), dtype=np.float64)
+    sc = (1.0 / np.sqrt(D)) if scale is None else scale
+    rc = lib().oracle_attention(_p(q), _p(kc), _p(vc), _p(kt), _p(vt), _p(mk), _p(ln), int(lmax), cap,
+                                _p(st), B, T - 1, Hq, Hkv, D, float(sc), _p(out))
+    return rc, out
+
+
+def attention_row(q_row, k_cache_bh, v_cache_bh, k_tree_bh, v_tree_bh, mask_row, len_b: int,
+                  lmax: int, scale: float):
+    q_row = _c(q_row, np.float32)
+    D = q_row.shape[0]
+    kc, vc = _c(k_cache_bh, np.float32), _c(v_cache_bh, np.float32)
+    kt, vt = _c(k_tree_bh, np.float32), _c(v_tree_bh, np.float32)
+    mr = _c(mask_row, np.uint64)
+    out = np.zeros(D, dtype=np.float64)
+    lib().oracle_attention_row(_p(q_row), _p(kc), _p(vc), _p(kt), _p(vt), _p(mr), int(len_b), int(lmax),
+                               kt.shape[0], D, float(scale), _p(out))
+    return out
+
+
+def argmax(logits: np.ndarray):
+    x = _c(logits, np.float32)
+    V = x.shape[-1]
+    rows = x.size // V
+    am = np.zeros(rows, dtype=np.int32)
+    lib().oracle_argmax(_p(x), rows, V, _p(am))
+    return am.reshape(x.shape[:-1])
+
+
+def accept(amax, tree_tokens, parents, M: int, status=None):
+    am = _c(amax, np.int32).reshape(-1, M + 1)
+    tok = _c(tree_tokens, np.int32).reshape(-1, M + 1)
+    par = _c(parents, np.int32).reshape(-1, M + 1)
+    B = par.shape[0]
+    st = None if status is None else _c(status, np.int32)
+    al = np.zeros(B, dtype=np.int32)
+    path = np.zeros((B, M + 1), dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    lib().oracle_accept(_p(am), _p(tok), _p(par), _p(st), B, M, _p(al), _p(path), _p(bonus))
+    return al, path, bonus
+
+
+def commit(kv_main: np.ndarray, kv_branch: np.ndarray, M: int, tokens_main, tree_tokens, lens,
+           lmax: int, path, accept_len, status=None, want_pos_ids: bool = True):
+    """kv_main [L][2][B][Hkv][cap][...] and kv_branch [L][2][B][Hkv][T][...] of
+    any dtype (raw bytes are moved).  Works on copies; returns
+    (rc, kv_main', tokens_main', lens', lmax', pos_ids)."""
+    km = np.array(kv_main, copy=True, order="C")
+    kb = _c(kv_branch, kv_branch.dtype)
+    L, _, B, Hkv, cap = km.shape[:5]
+    row_bytes = km[0, 0, 0, 0, 0].nbytes if km.size else 0
+    tm = None if tokens_main is None else np.array(tokens_main, dtype=np.int32, copy=True, order="C")
+    tt = _c(tree_tokens, np.int32)
+    ln = np.array(lens, dtype=np.int32, copy=True)
+    lm = np.array([lmax], dtype=np.int32)
+    pos = np.zeros((B, cap), dtype=np.int32) if want_pos_ids else None
+    st = None if status is None else _c(status, np.int32)
+    rc = lib().oracle_commit(_p(km.view(np.uint8)), _p(kb.view(np.uint8)), L, B, Hkv, cap, row_bytes, M,
+                             _p(tm), _p(tt), _p(ln), _p(lm), _p(pos), _p(_c(path, np.int32)),
+                             _p(_c(accept_len, np.int32)), _p(st))
+    return rc, km, tm, ln, int(lm[0]), pos

@@ -1,0 +1,334 @@
+/*
+ * svt_oracle.c -- plain CPU oracle for tree-masked verification.
+ *
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline leg of the
+ * benchmark).  It is deliberately slow and literal: every function computes
+ * the definition it cites, node by node and element by element, with no
+ * blocking, fusion or reordering.  Floating point is double precision.
+ *
+ * Source tags used below:
+ *   [EP-ko] "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend
+ *           NPUs", gist.science Korean summary.
+ *   [EP-nl] same paper, gist.science Dutch summary.
+ *   [BSD]   "Batch Speculative Decoding Done Right", gist.science Korean summary.
+ */
+#include "svt_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Tree validation.                                                          */
+/* [EP-ko] §2 Methodology (accelerator-safe tree tensorization) and [EP-nl]  */
+/* §2.B: a dummy row at index 0 stands for the root, so every parent index   */
+/* lies in [0, M]; structural invariants (range, acyclicity) are checked     */
+/* before any kernel runs.  Reading: row 0 is the root and points at itself; */
+/* a node i >= 1 may not be its own parent; every chain must reach row 0.    */
+/* The code reported for a tree is the first failing check in the order      */
+/* ROOT, RANGE, CYCLE.                                                       */
+/* ------------------------------------------------------------------------ */
+static int validate_one(const int32_t* par, int32_t M) {
+  int32_t T = M + 1;
+  if (par[0] != 0) return ORACLE_ERR_TREE_ROOT;
+  for (int32_t i = 1; i < T; ++i) {
+    if (par[i] < 0 || par[i] > M || par[i] == i) return ORACLE_ERR_TREE_RANGE;
+  }
+  for (int32_t i = 1; i < T; ++i) {
+    /* A chain without a cycle visits at most M distinct non-root nodes. */
+    int32_t u = i, steps = 0;
+    while (u != 0 && steps <= M) {
+      u = par[u];
+      ++steps;
+    }
+    if (u != 0) return ORACLE_ERR_TREE_CYCLE;
+  }
+  return ORACLE_OK;
+}
+
+int oracle_validate(const int32_t* parents, int32_t B, int32_t M, int32_t* status) {
+  int first = ORACLE_OK;
+  for (int32_t b = 0; b < B; ++b) {
+    int s = validate_one(parents + (int64_t)b * (M + 1), M);
+    status[b] = s;
+    if (s != ORACLE_OK && first == ORACLE_OK) first = s;
+  }
+  return first;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ancestor mask and depth.                                                  */
+/* [EP-ko] §2 (fused tree-masked teacher): node u may attend node v only if  */
+/* v is an ancestor of u; [EP-nl] §2.C states the same rule for the 4D mask. */
+/* Reading: the relation is reflexive (u also sees itself) and the root row  */
+/* 0 is an ancestor of every node.  Bit j of word j/64 of row i is set iff   */
+/* j lies on the walk i -> parent(i) -> ... -> 0.  depth[i] = edges walked.  */
+/* ------------------------------------------------------------------------ */
+void oracle_mask(const int32_t* parents, int32_t B, int32_t M, const int32_t* status,
+                 uint64_t* mask, int32_t* depth) {
+  int32_t T = M + 1, W = (T + 63) / 64;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t* par = parents + (int64_t)b * T;
+    uint64_t* mb = mask + (int64_t)b * T * W;
+    int32_t* db = depth + (int64_t)b * T;
+    memset(mb, 0, sizeof(uint64_t) * (size_t)T * (size_t)W);
+    memset(db, 0, sizeof(int32_t) * (size_t)T);
+    if (status && status[b] != 0) continue;
+    for (int32_t i = 0; i < T; ++i) {
+      int32_t u = i, d = 0;
+      for (;;) {
+        mb[(int64_t)i * W + u / 64] |= (uint64_t)1 << (u % 64);
+        if (u == 0) break;
+        u = par[u];
+        ++d;
+      }
+      db[i] = d;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tree-verify attention.                                                    */
+/* [EP-ko] §2 / [EP-nl] §2.C: the teacher verifies every speculative node in */
+/* one batched forward pass; node i's query attends the committed prefix and */
+/* the tree nodes allowed by the ancestor mask.  Readings: softmax scale is  */
+/* a parameter (1/sqrt(D) by default); query head h uses KV head h/G with    */
+/* G = Hq/Hkv (contiguous groups); the prefix of sequence b occupies cache   */
+/* columns [lmax-len_b, lmax) (left padding, [BSD] §2 rectangular            */
+/* alignment).  Key order: prefix columns ascending, then tree rows          */
+/* ascending.  s = scale * q.k ; p = exp(s - max s) ; out = sum p v / sum p. */
+/* ------------------------------------------------------------------------ */
+void oracle_attention_row(const float* q_row, const float* k_cache_bh, const float* v_cache_bh,
+                          const float* k_tree_bh, const float* v_tree_bh, const uint64_t* mask_row,
+                          int32_t len_b, int32_t lmax, int32_t T, int32_t D, double scale,
+                          double* out) {
+  int32_t n_tree = 0;
+  for (int32_t j = 0; j < T; ++j)
+    if ((mask_row[j / 64] >> (j % 64)) & 1u) ++n_tree;
+  int64_t n_keys = (int64_t)len_b + n_tree;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
+  const float** vrow = (const float**)malloc(sizeof(float*) * (size_t)(n_keys > 0 ? n_keys : 1));
+  int64_t n = 0;
+  /* prefix keys */
+  for (int32_t c = lmax - len_b; c < lmax; ++c) {
+    const float* k = k_cache_bh + (int64_t)c * D;
+    double acc = 0.0;
+    for (int32_t d = 0; d < D; ++d) acc += (double)q_row[d] * (double)k[d];
+    s[n] = scale * acc;
+    vrow[n] = v_cache_bh + (int64_t)c * D;
+    ++n;
+  }
+  /* tree keys allowed by the mask */
+  for (int32_t j = 0; j < T; ++j) {
+    if (!((mask_row[j / 64] >> (j % 64)) & 1u)) continue;
+    const float* k = k_tree_bh + (int64_t)j * D;
+    double acc = 0.0;
+    for (int32_t d = 0; d < D; ++d) acc += (double)q_row[d] * (double)k[d];
+    s[n] = scale * acc;
+    vrow[n] = v_tree_bh + (int64_t)j * D;
+    ++n;
+  }
+  for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
+  if (n == 0) {
+    free(s);
+    free(vrow);
+    return;
+  }
+  double m = s[0];
+  for (int64_t x = 1; x < n; ++x)
+    if (s[x] > m) m = s[x];
+  double l = 0.0;
+  for (int64_t x = 0; x < n; ++x) {
+    s[x] = exp(s[x] - m);
+    l += s[x];
+  }
+  for (int64_t x = 0; x < n; ++x)
+    for (int32_t d = 0; d < D; ++d) out[d] += s[x] * (double)vrow[x][d];
+  for (int32_t d = 0; d < D; ++d) out[d] /= l;
+  free(s);
+  free(vrow);
+}
+
+int oracle_attention(const float* q, const float* k_cache, const float* v_cache,
+                     const float* k_tree, const float* v_tree, const uint64_t* mask,
+                     const int32_t* len, int32_t lmax, int64_t cap, const int32_t* status,
+                     int32_t B, int32_t M, int32_t Hq, int32_t Hkv, int32_t D, double scale,
+                     double* out) {
+  int32_t T = M + 1, W = (T + 63) / 64, G = Hq / Hkv;
+  int rc = ORACLE_OK;
+  for (int32_t b = 0; b < B; ++b) {
+    int bad_len = (lmax < 0 || (int64_t)lmax > cap || len[b] < 0 || len[b] > lmax);
+    if (bad_len) rc = ORACLE_ERR_LENGTH;
+    for (int32_t i = 0; i < T; ++i) {
+      for (int32_t h = 0; h < Hq; ++h) {
+        double* o = out + (((int64_t)b * T + i) * Hq + h) * D;
+        if (bad_len || (status && status[b] != 0)) {
+          for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+          continue;
+        }
+        int32_t g = h / G;
+        oracle_attention_row(q + (((int64_t)b * T + i) * Hq + h) * D,
+                             k_cache + ((int64_t)b * Hkv + g) * cap * D,
+                             v_cache + ((int64_t)b * Hkv + g) * cap * D,
+                             k_tree + ((int64_t)b * Hkv + g) * T * D,
+                             v_tree + ((int64_t)b * Hkv + g) * T * D,
+                             mask + ((int64_t)b * T + i) * W, len[b], lmax, T, D, scale, o);
+      }
+    }
+  }
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Greedy argmax.  The teacher's greedy choice at a node is the vocabulary   */
+/* entry with the largest logit ([EP-ko] §4 compares against teacher-only    */
+/* greedy decoding).  Readings: ties go to the lowest index; a NaN ranks     */
+/* above every number and the first NaN wins; -0.0 equals +0.0.              */
+/* ------------------------------------------------------------------------ */
+static int ranks_above(float a, float b) {
+  if (isnan(a)) return !isnan(b);
+  if (isnan(b)) return 0;
+  return a > b;
+}
+
+void oracle_argmax(const float* logits, int64_t rows, int32_t V, int32_t* amax) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* x = logits + r * V;
+    int32_t best = 0;
+    for (int32_t v = 1; v < V; ++v)
+      if (ranks_above(x[v], x[best])) best = v;
+    amax[r] = best;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Acceptance.  A draft node i >= 1 is correct when its token equals the     */
+/* teacher's greedy token at its parent; the root is always accepted.  A     */
+/* node is accepted when every node on its root path is correct.  The        */
+/* accepted node of greatest depth (lowest index on ties) ends the accepted  */
+/* path; accept_len is its depth (the number of accepted draft tokens,       */
+/* [EP-ko] §4 accept_L), path[k] is its ancestor at depth k (zero padded:    */
+/* no negative sentinels, [EP-ko] §2), and the bonus token is the teacher's  */
+/* greedy token at the end node.  Sequences with a nonzero status accept     */
+/* nothing: accept_len 0, path all 0, bonus = greedy token at the root.      */
+/* ------------------------------------------------------------------------ */
+void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_t* parents,
+                   const int32_t* status, int32_t B, int32_t M,
+                   int32_t* accept_len, int32_t* path, int32_t* bonus) {
+  int32_t T = M + 1;
+  int32_t* dep = (int32_t*)malloc(sizeof(int32_t) * (size_t)T);
+  int* acc = (int*)malloc(sizeof(int) * (size_t)T);
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t* par = parents + (int64_t)b * T;
+    const int32_t* am = amax + (int64_t)b * T;
+    const int32_t* tok = tree_tokens + (int64_t)b * T;
+    int32_t* pb = path + (int64_t)b * T;
+    for (int32_t k = 0; k < T; ++k) pb[k] = 0;
+    if (status && status[b] != 0) {
+      accept_len[b] = 0;
+      bonus[b] = am[0];
+      continue;
+    }
+    for (int32_t i = 0; i < T; ++i) {
+      int32_t u = i, d = 0, all_ok = 1;
+      while (u != 0 && d <= M) { /* a valid tree reaches the root within M steps */
+        if (tok[u] != am[par[u]]) all_ok = 0;
+        u = par[u];
+        ++d;
+      }
+      dep[i] = d;
+      acc[i] = all_ok;
+    }
+    int32_t end = 0;
+    for (int32_t i = 1; i < T; ++i)
+      if (acc[i] && dep[i] > dep[end]) end = i;
+    accept_len[b] = dep[end];
+    for (int32_t u = end; ; u = par[u]) {
+      pb[dep[u]] = u;
+      if (u == 0) break;
+    }
+    bonus[b] = am[end];
+  }
+  free(dep);
+  free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Commit.  [BSD] §2: after a verify round each sequence keeps its old       */
+/* content and appends what it accepted (unpad, append, repad), so that      */
+/* padding + content equals the batch maximum for every sequence             */
+/* (rectangular alignment) and position ids run from 0 over the content.     */
+/* [EP-ko] §2 / [EP-nl] §2.A: the accepted rows come from the branch cache   */
+/* by path index, and only the new segment is reordered.                     */
+/* Readings: the committed rows are the root plus the accepted drafts        */
+/* (A_b = accept_len_b + 1 rows: path[b][0..A_b)); sequences with a nonzero  */
+/* status append nothing but still follow the new alignment; padding sits on */
+/* the left; pos_ids padding is 0; columns >= new lmax are left untouched.   */
+/* ------------------------------------------------------------------------ */
+int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, int32_t B,
+                  int32_t Hkv, int64_t cap, int32_t row_bytes, int32_t M,
+                  int32_t* tokens_main, const int32_t* tree_tokens, int32_t* len, int32_t* lmax,
+                  int32_t* pos_ids, const int32_t* path, const int32_t* accept_len,
+                  const int32_t* status) {
+  int32_t T = M + 1;
+  int32_t old_lmax = *lmax;
+  if (old_lmax < 0 || (int64_t)old_lmax > cap) return ORACLE_ERR_ARG;
+  int32_t* A = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+  int32_t new_lmax = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (len[b] < 0 || len[b] > old_lmax) { free(A); return ORACLE_ERR_ARG; }
+    int valid = !(status && status[b] != 0);
+    if (valid && (accept_len[b] < 0 || accept_len[b] > M)) { free(A); return ORACLE_ERR_ARG; }
+    A[b] = valid ? accept_len[b] + 1 : 0;
+    if (valid)
+      for (int32_t k = 0; k < A[b]; ++k)
+        if (path[(int64_t)b * T + k] < 0 || path[(int64_t)b * T + k] > M) { free(A); return ORACLE_ERR_ARG; }
+    if (len[b] + A[b] > new_lmax) new_lmax = len[b] + A[b];
+  }
+  if ((int64_t)new_lmax > cap) { free(A); return ORACLE_ERR_CAPACITY; }
+
+  /* Per sequence: build the logical row list (old content, then the accepted
+   * branch rows in path order), then write it back left-padded to new_lmax. */
+  uint8_t* tmp = (uint8_t*)malloc((size_t)(new_lmax > 0 ? new_lmax : 1) * (size_t)row_bytes);
+  for (int32_t l = 0; l < n_layers; ++l)
+    for (int32_t kv = 0; kv < 2; ++kv)
+      for (int32_t b = 0; b < B; ++b)
+        for (int32_t h = 0; h < Hkv; ++h) {
+          int64_t slab = (((int64_t)l * 2 + kv) * B + b) * Hkv + h;
+          uint8_t* main_s = kv_main + slab * cap * row_bytes;
+          const uint8_t* br_s = kv_branch + slab * (int64_t)T * row_bytes;
+          int32_t old_pad = old_lmax - len[b];
+          int32_t n = 0;
+          for (int32_t c = old_pad; c < old_lmax; ++c, ++n)
+            memcpy(tmp + (int64_t)n * row_bytes, main_s + (int64_t)c * row_bytes, (size_t)row_bytes);
+          for (int32_t k = 0; k < A[b]; ++k, ++n)
+            memcpy(tmp + (int64_t)n * row_bytes, br_s + (int64_t)path[(int64_t)b * T + k] * row_bytes,
+                   (size_t)row_bytes);
+          int32_t new_pad = new_lmax - n;
+          memcpy(main_s + (int64_t)new_pad * row_bytes, tmp, (size_t)n * (size_t)row_bytes);
+        }
+  free(tmp);
+
+  int32_t* ttmp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(new_lmax > 0 ? new_lmax : 1));
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t new_len = len[b] + A[b];
+    int32_t new_pad = new_lmax - new_len;
+    if (tokens_main) {
+      int32_t* tm = tokens_main + (int64_t)b * cap;
+      int32_t n = 0;
+      for (int32_t c = old_lmax - len[b]; c < old_lmax; ++c) ttmp[n++] = tm[c];
+      for (int32_t k = 0; k < A[b]; ++k)
+        ttmp[n++] = tree_tokens[(int64_t)b * T + path[(int64_t)b * T + k]];
+      for (int32_t x = 0; x < n; ++x) tm[new_pad + x] = ttmp[x];
+    }
+    if (pos_ids) {
+      int32_t* pp = pos_ids + (int64_t)b * cap;
+      for (int32_t c = 0; c < new_lmax; ++c) pp[c] = c < new_pad ? 0 : c - new_pad;
+    }
+  }
+  free(ttmp);
+  for (int32_t b = 0; b < B; ++b) len[b] += A[b];
+  *lmax = new_lmax;
+  free(A);
+  return ORACLE_OK;
+}

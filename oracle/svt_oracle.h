@@ -1,0 +1,102 @@
+/*
+ * svt_oracle.h -- CPU oracle for the tree-verification step of tree speculative
+ * decoding.  TEST INFRASTRUCTURE ONLY: this library exists so that the tests,
+ * the smoke check and the CPU-baseline leg of the benchmark can check the GPU
+ * library against plain definitions.  Nothing in the product path may link,
+ * load or call it.
+ *
+ * It shares no code, header, table or constant with the GPU library.  The
+ * status numbers below are written out again here on purpose: both sides
+ * follow the same documented code table, and a test compares the numbers.
+ *
+ * Every function works on host memory, in the plainest form of the
+ * definition it implements; floating-point work is done in double precision.
+ *
+ * Sources (the pages are summaries of two papers):
+ *   [EP-ko] "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend
+ *           NPUs", gist.science Korean summary page.
+ *   [EP-nl] the same paper, gist.science Dutch summary page.
+ *   [BSD]   "Batch Speculative Decoding Done Right", gist.science Korean
+ *           summary page.
+ */
+#ifndef SVT_ORACLE_H
+#define SVT_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_TREE_ROOT (-3)
+#define ORACLE_ERR_TREE_RANGE (-4)
+#define ORACLE_ERR_TREE_CYCLE (-5)
+#define ORACLE_ERR_CAPACITY (-6)
+#define ORACLE_ERR_LENGTH (-9)
+
+/* Tree validation ([EP-ko] §2 Methodology, accelerator-safe tree tensorization;
+ * [EP-nl] §2.B dummy-root indexing and invariant checks).
+ * parents: [B][M+1].  status: [B] out.  Returns the first nonzero status, or 0. */
+int oracle_validate(const int32_t* parents, int32_t B, int32_t M, int32_t* status);
+
+/* Ancestor mask and depth ([EP-ko] §2, fused tree-masked teacher: u attends v
+ * only when v is an ancestor of u; reflexive reading).  mask: [B][T][W] with
+ * W = ceil(T/64); depth: [B][T].  Sequences whose status is nonzero get all
+ * zeros.  status may be NULL (then every tree must be valid). */
+void oracle_mask(const int32_t* parents, int32_t B, int32_t M, const int32_t* status,
+                 uint64_t* mask, int32_t* depth);
+
+/* Tree-verify attention ([EP-ko] §2 fused tree-masked teacher execution;
+ * [EP-nl] §2.C).  All tensors are float (exact upcasts of what the GPU reads);
+ * the result is double.
+ *   q      [B][T][Hq][D]
+ *   k_cache, v_cache [B][Hkv][cap][D]   content of b in columns [lmax-len_b, lmax)
+ *   k_tree, v_tree   [B][Hkv][T][D]
+ *   mask   [B][T][W]
+ *   out    [B][T][Hq][D] (double)
+ * Sequences with nonzero status, or with inconsistent lengths, get zeros.
+ * Returns 0, or ORACLE_ERR_LENGTH when some sequence had inconsistent lengths. */
+int oracle_attention(const float* q, const float* k_cache, const float* v_cache,
+                     const float* k_tree, const float* v_tree, const uint64_t* mask,
+                     const int32_t* len, int32_t lmax, int64_t cap, const int32_t* status,
+                     int32_t B, int32_t M, int32_t Hq, int32_t Hkv, int32_t D, double scale,
+                     double* out);
+
+/* Attention for a single (b, head, node) triple, same definition as above; used
+ * for sampled checks of large instances. out: [D]. */
+void oracle_attention_row(const float* q_row, const float* k_cache_bh, const float* v_cache_bh,
+                          const float* k_tree_bh, const float* v_tree_bh, const uint64_t* mask_row,
+                          int32_t len_b, int32_t lmax, int32_t T, int32_t D, double scale,
+                          double* out);
+
+/* Greedy argmax per row, lowest index on ties, first NaN wins. */
+void oracle_argmax(const float* logits, int64_t rows, int32_t V, int32_t* amax);
+
+/* Greedy acceptance of the longest root path ([EP-ko] §4 Results, accepted
+ * length accept_L; greedy teacher rule).  Works from the parent array alone.
+ *   amax [B][T] in (from oracle_argmax), tree_tokens [B][T], parents [B][T]
+ *   accept_len [B], path [B][T], bonus [B] out. */
+void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_t* parents,
+                   const int32_t* status, int32_t B, int32_t M,
+                   int32_t* accept_len, int32_t* path, int32_t* bonus);
+
+/* KV commit with EQSPEC re-padding ([BSD] §2 Methodology: rectangular
+ * alignment, position-id contiguity, unpad-append-repad; [EP-ko] §2 fast
+ * reorder by path_indices; [EP-nl] §2.A commit modes).
+ *   kv_main   [L][2][B][Hkv][cap][row_bytes]  in/out (raw bytes)
+ *   kv_branch [L][2][B][Hkv][T][row_bytes]
+ *   tokens_main [B][cap] in/out (nullable), tree_tokens [B][T]
+ *   len [B], lmax [1] in/out, pos_ids [B][cap] out (nullable)
+ * Returns 0, ORACLE_ERR_ARG or ORACLE_ERR_CAPACITY; on error nothing changes. */
+int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, int32_t B,
+                  int32_t Hkv, int64_t cap, int32_t row_bytes, int32_t M,
+                  int32_t* tokens_main, const int32_t* tree_tokens, int32_t* len, int32_t* lmax,
+                  int32_t* pos_ids, const int32_t* path, const int32_t* accept_len,
+                  const int32_t* status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
