@@ -1,0 +1,220 @@
+/*
+ * svt.h -- tree-masked speculative verification on AMD Instinct MI355X (gfx950).
+ *
+ * One verification round of tree speculative decoding, batched over ragged
+ * sequences, as four calls:
+ *
+ *   svt_build_mask        validate parent arrays, build ancestor bitmasks + depth
+ *   svt_verify_attention  attention of every tree node over prefix KV + tree KV
+ *   svt_accept            greedy argmax per node, longest accepted root path
+ *   svt_commit            append the accepted rows to the main cache, re-pad
+ *
+ * Sources (summary pages of two papers):
+ *   [EP-ko] "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend
+ *           NPUs", gist.science Korean summary.
+ *   [EP-nl] the same paper, gist.science Dutch summary.
+ *   [BSD]   "Batch Speculative Decoding Done Right", gist.science Korean summary.
+ *
+ * Conventions shared by every call
+ *   - Pointers are device memory owned by the caller unless the name ends in
+ *     _host.  The library keeps no state between calls.  Calls that need
+ *     scratch memory take a caller-provided workspace whose size a *_workspace
+ *     query returns; the library itself allocates nothing.
+ *   - Every call enqueues its kernels on the caller's stream and returns at once,
+ *     except where SVT_SYNC_CHECK is given (then it synchronises that stream).
+ *   - The return value is SVT_OK or a negative svt_status.  Argument errors are
+ *     found on the host before anything is launched and leave every buffer
+ *     untouched.  Tree errors are found on the device and reported per sequence
+ *     through a status array.
+ *   - Index arrays never hold negative values: the tree root is a dummy row 0
+ *     that points at itself, and padding entries of index outputs are 0
+ *     ([EP-ko] section 2, accelerator-safe tree tensorization; [EP-nl] 2.B).
+ *   - T = M + 1 rows per tree (row 0 = root, rows 1..M = draft nodes), at most
+ *     SVT_MAX_T.  W = ceil(T / 64) mask words per row.  G = Hq / Hkv.
+ *   - bf16 tensors hold raw bfloat16 bits; fp32 tensors hold IEEE binary32.
+ */
+#ifndef SVT_H
+#define SVT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVT_MAX_T 256 /* M <= 255, W <= 4 */
+
+typedef enum svt_status {
+  SVT_OK = 0,
+  SVT_ERR_ARG = -1,          /* bad pointer, size or layout (host check)              */
+  SVT_ERR_UNSUPPORTED = -2,  /* valid but not implemented: head dim, dtype, T          */
+  SVT_ERR_TREE_ROOT = -3,    /* parents[b][0] != 0                                     */
+  SVT_ERR_TREE_RANGE = -4,   /* some parents[b][i], i >= 1, outside [0, M] or == i     */
+  SVT_ERR_TREE_CYCLE = -5,   /* some node's parent chain never reaches row 0           */
+  SVT_ERR_CAPACITY = -6,     /* commit would need more than cap cache columns          */
+  SVT_ERR_WORKSPACE = -7,    /* workspace pointer missing or too small                 */
+  SVT_ERR_HIP = -8,          /* a HIP runtime call failed                               */
+  SVT_ERR_LENGTH = -9        /* device lengths inconsistent (len > lmax, lmax > bound)  */
+} svt_status;
+
+typedef enum svt_dtype { SVT_FP32 = 0, SVT_BF16 = 1 } svt_dtype;
+
+/* Flag: after enqueueing, synchronise the stream and return the first nonzero
+ * device status the call produced (tree status for svt_build_mask, commit status
+ * for svt_commit). */
+#define SVT_SYNC_CHECK 1
+
+/* ------------------------------------------------------------------------ */
+/* svt_build_mask                                                            */
+/* Validates each tree and builds its ancestor mask.                         */
+/*   Validation ([EP-ko] section 2, tree tensorization with structural       */
+/*   checks before kernels run; [EP-nl] 2.B invariant checks): status[b] =   */
+/*   SVT_ERR_TREE_ROOT if parents[b][0] != 0, else SVT_ERR_TREE_RANGE if some */
+/*   i >= 1 has parents[b][i] outside [0, M] or equal to i, else              */
+/*   SVT_ERR_TREE_CYCLE if some chain never reaches row 0, else SVT_OK.       */
+/*   Mask ([EP-ko] section 2, fused tree-masked teacher; [EP-nl] 2.C): node u */
+/*   may attend v only if v is u itself or an ancestor of u.  Bit (j % 64) of */
+/*   mask[b][i][j / 64] is 1 iff j is i or an ancestor of i (root included);  */
+/*   unused high bits are 0.  depth[b][i] = number of edges from i to row 0.  */
+/*   Invalid trees get all-zero mask and depth rows.                          */
+/* Arguments                                                                  */
+/*   parents [B][T] int32 in; mask [B][T][W] uint64 out; depth [B][T] int32   */
+/*   out; status [B] int32 out.  B >= 0, 0 <= M < SVT_MAX_T.                  */
+/* Returns SVT_OK, SVT_ERR_ARG / SVT_ERR_UNSUPPORTED (host), SVT_ERR_HIP, or  */
+/* with SVT_SYNC_CHECK the first nonzero status[b].                           */
+/* ------------------------------------------------------------------------ */
+int svt_build_mask(const int32_t* parents, int32_t B, int32_t M, uint64_t* mask, int32_t* depth,
+                   int32_t* status, int32_t flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* svt_verify_attention                                                      */
+/* One batched attention pass over all tree nodes ([EP-ko] section 2, fused  */
+/* tree-masked teacher execution; [EP-nl] 2.C).  For sequence b, query head  */
+/* h (KV head g = h / G) and node i:                                          */
+/*   keys = prefix cache columns [lmax - len[b], lmax) of k_cache[b][g]       */
+/*          plus tree rows j of k_tree[b][g] with mask bit j of row i set     */
+/*   out[b][i][h] = softmax(scale * q[b][i][h] . key) weighted sum of values  */
+/* The prefix is left padded: every sequence's content ends at column lmax    */
+/* ([BSD] section 2, rectangular alignment).  Columns outside the content are */
+/* never read.  Accumulation and softmax are fp32; bf16 inputs use bf16 MFMA  */
+/* for both contractions (probabilities are rounded to bf16 for the second).  */
+/* The result is bitwise deterministic run to run.                            */
+/* ------------------------------------------------------------------------ */
+typedef struct svt_attn_args {
+  int32_t B, M, Hq, Hkv, D;  /* D in {64, 128}; Hq % Hkv == 0                        */
+  int32_t dtype;             /* svt_dtype of q, caches, tree KV and out               */
+  float scale;               /* softmax scale; 0 selects 1 / sqrt(D)                  */
+  const void* q;             /* [B][T][Hq][D]                                         */
+  const void* k_cache;       /* [B][Hkv][cap][D], one layer                           */
+  const void* v_cache;       /* [B][Hkv][cap][D]                                      */
+  int64_t cap;               /* cache columns                                         */
+  const int32_t* len;        /* [B] device: content length per sequence              */
+  const int32_t* lmax;       /* [1] device: batch length; content ends here           */
+  int32_t lmax_bound;        /* host upper bound on *lmax, sizes the grid; <= cap     */
+  const void* k_tree;        /* [B][Hkv][T][D] the tree's own (branch) keys           */
+  const void* v_tree;        /* [B][Hkv][T][D]                                        */
+  const uint64_t* mask;      /* [B][T][W] from svt_build_mask                         */
+  const int32_t* status;     /* [B] from svt_build_mask, or NULL (all valid)          */
+  void* out;                 /* [B][T][Hq][D], dtype of q                             */
+  int32_t* seq_status;       /* [B] out, or NULL: SVT_OK, the tree status, or         */
+                             /* SVT_ERR_LENGTH if 0 <= len[b] <= lmax <= lmax_bound   */
+                             /* fails.  Such sequences get all-zero output.           */
+  void* workspace;           /* device scratch, svt_verify_attention_workspace bytes  */
+  size_t workspace_bytes;
+} svt_attn_args;
+
+/* Bytes of workspace svt_verify_attention needs for these shapes (pointer
+ * fields are ignored).  0 for invalid arguments. */
+size_t svt_verify_attention_workspace(const svt_attn_args* a);
+int svt_verify_attention(const svt_attn_args* a, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* svt_accept                                                                */
+/* Greedy verification ([EP-ko] section 4: accepted length accept_L under    */
+/* the teacher's greedy choice).                                              */
+/*   amax[b][i]   = index of the largest logits[b][i][v]; lowest index on     */
+/*                  ties; a NaN ranks above every number (first NaN wins);    */
+/*                  -0.0 equals +0.0.                                         */
+/*   ok(i)        = i == 0, or tree_tokens[b][i] == amax[b][parents[b][i]]    */
+/*   accepted(i)  = ok holds on every node of i's root path (mask row i)      */
+/*   end          = accepted node of greatest depth, lowest index on ties     */
+/*   accept_len[b]= depth[b][end] (accepted draft tokens, root excluded)      */
+/*   path[b][k]   = ancestor of end at depth k for k <= accept_len, else 0    */
+/*   bonus[b]     = amax[b][end]                                              */
+/* Sequences with status[b] != 0 accept nothing: accept_len 0, path 0,        */
+/* bonus = amax[b][0].                                                        */
+/* ------------------------------------------------------------------------ */
+typedef struct svt_accept_args {
+  int32_t B, M, V;
+  const float* logits;         /* [B][T][V] fp32                                    */
+  const int32_t* tree_tokens;  /* [B][T] draft token of each node (root: any)        */
+  const int32_t* parents;      /* [B][T]                                             */
+  const uint64_t* mask;        /* [B][T][W] from svt_build_mask                      */
+  const int32_t* depth;        /* [B][T] from svt_build_mask                         */
+  const int32_t* status;       /* [B] or NULL                                        */
+  int32_t* amax;               /* [B][T] out                                         */
+  int32_t* accept_len;         /* [B] out                                            */
+  int32_t* path;               /* [B][T] out (the path_indices of the commit)        */
+  int32_t* bonus;              /* [B] out                                            */
+  void* workspace;             /* device scratch, svt_accept_workspace bytes         */
+  size_t workspace_bytes;
+} svt_accept_args;
+
+size_t svt_accept_workspace(const svt_accept_args* a);
+int svt_accept(const svt_accept_args* a, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* svt_commit                                                                */
+/* Unpad-append-repad of the main cache after a round ([BSD] section 2:       */
+/* rectangular alignment and position ids contiguous from 0; [EP-ko]          */
+/* section 2: accepted rows gathered from the branch cache by path index,     */
+/* only the new segment reordered; [EP-nl] 2.A commit modes).                 */
+/*   A_b   = accept_len[b] + 1 (root + accepted drafts), or 0 when status[b]  */
+/*           is nonzero                                                       */
+/*   len'  = len + A,  lmax' = max_b len'_b,  pad'_b = lmax' - len'_b         */
+/*   Sequence b's old content [lmax - len_b, lmax) moves to                   */
+/*   [pad'_b, pad'_b + len_b); rows path[b][0..A_b) of kv_branch follow at    */
+/*   [pad'_b + len_b, lmax').  Same for every layer, K and V plane and KV     */
+/*   head, and for tokens_main (with tree_tokens[b][path[b][k]]).             */
+/*   pos_ids[b][c] = c - pad'_b on content, 0 on padding, for c < lmax'.      */
+/*   Columns >= lmax' are not written; padding contents are unspecified.      */
+/* Rows are moved as raw bytes (any bit pattern survives).  If lmax' > cap,   */
+/* or the device-side arguments are inconsistent, nothing is written and      */
+/* commit_status says why.  len and lmax are updated in place.                */
+/* ------------------------------------------------------------------------ */
+typedef struct svt_commit_args {
+  int32_t B, M, Hkv, D, n_layers;
+  int32_t dtype;               /* svt_dtype (element size of cache rows)            */
+  int64_t cap;
+  void* kv_main;               /* [n_layers][2][B][Hkv][cap][D] in/out              */
+  const void* kv_branch;       /* [n_layers][2][B][Hkv][T][D]                        */
+  int32_t* tokens_main;        /* [B][cap] in/out, or NULL                           */
+  const int32_t* tree_tokens;  /* [B][T] (needed when tokens_main is set)            */
+  int32_t* len;                /* [B] in/out                                         */
+  int32_t* lmax;               /* [1] in/out                                         */
+  int32_t* pos_ids;            /* [B][cap] out, or NULL                              */
+  const int32_t* path;         /* [B][T] from svt_accept                             */
+  const int32_t* accept_len;   /* [B] from svt_accept                                */
+  const int32_t* status;       /* [B] or NULL                                        */
+  int32_t* commit_status;      /* [1] out: SVT_OK, SVT_ERR_CAPACITY or SVT_ERR_LENGTH */
+} svt_commit_args;
+
+int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Utilities                                                                  */
+/* ------------------------------------------------------------------------ */
+/* Synchronises the stream, copies n int32 statuses to the host and returns the
+ * first nonzero one (SVT_OK if none, SVT_ERR_HIP on a runtime failure). */
+int svt_check_status(const int32_t* status, int32_t n, hipStream_t stream);
+const char* svt_status_string(int code);
+/* Library version, e.g. "0.1.0 gfx950". */
+const char* svt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVT_H */

@@ -272,19 +272,29 @@ int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, 
                   const int32_t* status) {
   int32_t T = M + 1;
   int32_t old_lmax = *lmax;
-  if (old_lmax < 0 || (int64_t)old_lmax > cap) return ORACLE_ERR_ARG;
+  /* Inconsistent lengths are reported before bad accept results, which are
+   * reported before a capacity overflow; in every case nothing changes. */
+  if (old_lmax < 0 || (int64_t)old_lmax > cap) return ORACLE_ERR_LENGTH;
+  for (int32_t b = 0; b < B; ++b)
+    if (len[b] < 0 || len[b] > old_lmax) return ORACLE_ERR_LENGTH;
   int32_t* A = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
   int32_t new_lmax = 0;
+  int arg_bad = 0;
   for (int32_t b = 0; b < B; ++b) {
-    if (len[b] < 0 || len[b] > old_lmax) { free(A); return ORACLE_ERR_ARG; }
     int valid = !(status && status[b] != 0);
-    if (valid && (accept_len[b] < 0 || accept_len[b] > M)) { free(A); return ORACLE_ERR_ARG; }
-    A[b] = valid ? accept_len[b] + 1 : 0;
-    if (valid)
-      for (int32_t k = 0; k < A[b]; ++k)
-        if (path[(int64_t)b * T + k] < 0 || path[(int64_t)b * T + k] > M) { free(A); return ORACLE_ERR_ARG; }
+    A[b] = 0;
+    if (valid) {
+      if (accept_len[b] < 0 || accept_len[b] > M) {
+        arg_bad = 1;
+      } else {
+        A[b] = accept_len[b] + 1;
+        for (int32_t k = 0; k < A[b]; ++k)
+          if (path[(int64_t)b * T + k] < 0 || path[(int64_t)b * T + k] > M) arg_bad = 1;
+      }
+    }
     if (len[b] + A[b] > new_lmax) new_lmax = len[b] + A[b];
   }
+  if (arg_bad) { free(A); return ORACLE_ERR_ARG; }
   if ((int64_t)new_lmax > cap) { free(A); return ORACLE_ERR_CAPACITY; }
 
   /* Per sequence: build the logical row list (old content, then the accepted

@@ -89,7 +89,9 @@ void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_
  *   kv_branch [L][2][B][Hkv][T][row_bytes]
  *   tokens_main [B][cap] in/out (nullable), tree_tokens [B][T]
  *   len [B], lmax [1] in/out, pos_ids [B][cap] out (nullable)
- * Returns 0, ORACLE_ERR_ARG or ORACLE_ERR_CAPACITY; on error nothing changes. */
+ * Returns 0, or on error (nothing changes) ORACLE_ERR_LENGTH for inconsistent
+ * lengths, ORACLE_ERR_ARG for an accept length or path entry outside [0, M],
+ * ORACLE_ERR_CAPACITY when the new lmax would exceed cap (checked in that order). */
 int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, int32_t B,
                   int32_t Hkv, int64_t cap, int32_t row_bytes, int32_t M,
                   int32_t* tokens_main, const int32_t* tree_tokens, int32_t* len, int32_t* lmax,

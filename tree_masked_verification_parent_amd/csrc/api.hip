@@ -1,0 +1,156 @@
+// C-ABI entry points of libsvt: host-side argument checks, launch, tracing.
+// Every device step runs in the kernels of mask.hip, attn.hip, accept.hip and
+// commit.hip; this file only validates, sizes and enqueues.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "svt_internal.h"
+
+namespace {
+
+bool trace_on() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = std::getenv("SVT_TRACE");
+    on = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return on == 1;
+}
+
+int finish(const char* name, int rc, const char* shape) {
+  if (trace_on()) std::fprintf(stderr, "[svt] %s %s -> %d (%s)\n", name, shape, rc, svt_status_string(rc));
+  return rc;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? SVT_OK : SVT_ERR_HIP; }
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int svt_build_mask(const int32_t* parents, int32_t B, int32_t M, uint64_t* mask, int32_t* depth,
+                   int32_t* status, int32_t flags, hipStream_t stream) {
+  char shape[96];
+  std::snprintf(shape, sizeof shape, "B=%d M=%d", B, M);
+  if (B < 0 || M < 0) return finish("svt_build_mask", SVT_ERR_ARG, shape);
+  if (M >= SVT_MAX_T) return finish("svt_build_mask", SVT_ERR_UNSUPPORTED, shape);
+  if (B == 0) return finish("svt_build_mask", SVT_OK, shape);
+  if (!parents || !mask || !depth || !status || !aligned(mask, 8)) return finish("svt_build_mask", SVT_ERR_ARG, shape);
+  int rc = hip_rc(svt::launch_build_mask(parents, B, M, mask, depth, status, stream));
+  if (rc == SVT_OK && (flags & SVT_SYNC_CHECK)) rc = svt_check_status(status, B, stream);
+  return finish("svt_build_mask", rc, shape);
+}
+
+size_t svt_verify_attention_workspace(const svt_attn_args* a) {
+  svt::AttnPlan p;
+  if (!svt::plan_attention(a, &p)) return 0;
+  return p.ws_bytes;
+}
+
+int svt_verify_attention(const svt_attn_args* a, hipStream_t stream) {
+  char shape[160];
+  if (!a) return finish("svt_verify_attention", SVT_ERR_ARG, "null args");
+  std::snprintf(shape, sizeof shape, "B=%d M=%d Hq=%d Hkv=%d D=%d dtype=%d cap=%lld lmax_bound=%d", a->B, a->M,
+                a->Hq, a->Hkv, a->D, a->dtype, (long long)a->cap, a->lmax_bound);
+  if (a->B < 0 || a->M < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0 || a->cap < 0 ||
+      a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap || !(a->scale >= 0.0f))
+    return finish("svt_verify_attention", SVT_ERR_ARG, shape);
+  if (a->M >= SVT_MAX_T || (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
+    return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);
+  if (a->B == 0) return finish("svt_verify_attention", SVT_OK, shape);
+  if (!a->q || !a->k_cache || !a->v_cache || !a->len || !a->lmax || !a->k_tree || !a->v_tree || !a->mask ||
+      !a->out)
+    return finish("svt_verify_attention", SVT_ERR_ARG, shape);
+  if (!aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->k_tree, 16) ||
+      !aligned(a->v_tree, 16) || !aligned(a->out, 16) || !aligned(a->mask, 8))
+    return finish("svt_verify_attention", SVT_ERR_ARG, shape);
+  svt::AttnPlan p;
+  if (!svt::plan_attention(a, &p)) return finish("svt_verify_attention", SVT_ERR_ARG, shape);
+  if (p.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < p.ws_bytes || !aligned(a->workspace, 16)))
+    return finish("svt_verify_attention", SVT_ERR_WORKSPACE, shape);
+  return finish("svt_verify_attention", hip_rc(svt::launch_attention(a, p, stream)), shape);
+}
+
+size_t svt_accept_workspace(const svt_accept_args* a) {
+  svt::AcceptPlan p;
+  if (!svt::plan_accept(a, &p)) return 0;
+  return p.ws_bytes;
+}
+
+int svt_accept(const svt_accept_args* a, hipStream_t stream) {
+  char shape[96];
+  if (!a) return finish("svt_accept", SVT_ERR_ARG, "null args");
+  std::snprintf(shape, sizeof shape, "B=%d M=%d V=%d", a->B, a->M, a->V);
+  if (a->B < 0 || a->M < 0 || a->V <= 0) return finish("svt_accept", SVT_ERR_ARG, shape);
+  if (a->M >= SVT_MAX_T) return finish("svt_accept", SVT_ERR_UNSUPPORTED, shape);
+  if (a->B == 0) return finish("svt_accept", SVT_OK, shape);
+  if (!a->logits || !a->tree_tokens || !a->parents || !a->mask || !a->depth || !a->amax || !a->accept_len ||
+      !a->path || !a->bonus || !aligned(a->mask, 8) || !aligned(a->logits, 4))
+    return finish("svt_accept", SVT_ERR_ARG, shape);
+  svt::AcceptPlan p;
+  if (!svt::plan_accept(a, &p)) return finish("svt_accept", SVT_ERR_ARG, shape);
+  if ((int64_t)p.rows * p.nchunk > 0x7FFFFFFF) return finish("svt_accept", SVT_ERR_UNSUPPORTED, shape);
+  if (!a->workspace || a->workspace_bytes < p.ws_bytes || !aligned(a->workspace, 8))
+    return finish("svt_accept", SVT_ERR_WORKSPACE, shape);
+  return finish("svt_accept", hip_rc(svt::launch_accept(a, p, stream)), shape);
+}
+
+int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream) {
+  char shape[128];
+  if (!a) return finish("svt_commit", SVT_ERR_ARG, "null args");
+  std::snprintf(shape, sizeof shape, "B=%d M=%d Hkv=%d D=%d layers=%d dtype=%d cap=%lld", a->B, a->M, a->Hkv, a->D,
+                a->n_layers, a->dtype, (long long)a->cap);
+  if (a->B < 0 || a->M < 0 || a->Hkv < 0 || a->D <= 0 || a->n_layers < 0 || a->cap < 0 || a->cap > 0x7FFFFFFF)
+    return finish("svt_commit", SVT_ERR_ARG, shape);
+  if (a->M >= SVT_MAX_T || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
+    return finish("svt_commit", SVT_ERR_UNSUPPORTED, shape);
+  const int esize = a->dtype == SVT_FP32 ? 4 : 2;
+  if ((a->D * esize) % 16 != 0) return finish("svt_commit", SVT_ERR_UNSUPPORTED, shape);
+  if (!a->len || !a->lmax || !a->path || !a->accept_len || !a->commit_status)
+    return finish("svt_commit", SVT_ERR_ARG, shape);
+  const bool has_kv = a->n_layers > 0 && a->Hkv > 0 && a->B > 0;
+  if (has_kv && (!a->kv_main || !a->kv_branch || !aligned(a->kv_main, 16) || !aligned(a->kv_branch, 16)))
+    return finish("svt_commit", SVT_ERR_ARG, shape);
+  if (a->tokens_main && !a->tree_tokens) return finish("svt_commit", SVT_ERR_ARG, shape);
+  int rc = hip_rc(svt::launch_commit(a, stream));
+  if (rc == SVT_OK && (flags & SVT_SYNC_CHECK)) rc = svt_check_status(a->commit_status, 1, stream);
+  return finish("svt_commit", rc, shape);
+}
+
+int svt_check_status(const int32_t* status, int32_t n, hipStream_t stream) {
+  if (n < 0 || (n > 0 && !status)) return SVT_ERR_ARG;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SVT_ERR_HIP;
+  if (n == 0) return SVT_OK;
+  int32_t small[64];
+  int32_t* host = n <= 64 ? small : static_cast<int32_t*>(std::malloc(sizeof(int32_t) * (size_t)n));
+  if (!host) return SVT_ERR_HIP;
+  int rc = SVT_OK;
+  if (hipMemcpy(host, status, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost) != hipSuccess) rc = SVT_ERR_HIP;
+  for (int32_t i = 0; rc == SVT_OK && i < n; ++i)
+    if (host[i] != SVT_OK) rc = host[i];
+  if (host != small) std::free(host);
+  return rc;
+}
+
+const char* svt_status_string(int code) {
+  switch (code) {
+    case SVT_OK: return "ok";
+    case SVT_ERR_ARG: return "invalid argument";
+    case SVT_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SVT_ERR_TREE_ROOT: return "tree: parents[0] is not 0";
+    case SVT_ERR_TREE_RANGE: return "tree: parent index out of [0, M] or self-parent";
+    case SVT_ERR_TREE_CYCLE: return "tree: a parent chain never reaches the root";
+    case SVT_ERR_CAPACITY: return "commit exceeds cache capacity";
+    case SVT_ERR_WORKSPACE: return "workspace missing or too small";
+    case SVT_ERR_HIP: return "HIP runtime error";
+    case SVT_ERR_LENGTH: return "inconsistent sequence lengths";
+    default: return "unknown status";
+  }
+}
+
+const char* svt_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,705 @@
+// Tree-verify attention: every tree node's query attends the left-padded
+// prefix KV cache plus the tree's own KV under the ancestor mask.
+//
+// Sources: EAGLE-Pangu (gist.science ko summary, section 2 Methodology: the
+// teacher verifies all speculative tokens in one batched forward with a 4D
+// tree mask, node u seeing node v only when v is an ancestor of u; fused
+// attention is the performance mode); the nl summary, section 2.C.  Left
+// padding of the prefix: Batch Speculative Decoding Done Right (ko summary,
+// section 2, rectangular alignment).
+//
+// Work decomposition (one launch covers the whole batch):
+//   * A KV head g of sequence b serves G = Hq/Hkv query heads, so its query
+//     rows are r = hl*T + i (hl < G, node i < T): R = G*T rows that all read
+//     the same keys.  This is what makes Q K^T and P V dense contractions.
+//   * Rows are cut into 16-row tiles; a workgroup (4 waves) owns a block of
+//     tiles, each wave `qw` of them (or 2 waves share one tile row-set and
+//     split each key tile when there are only 1-2 tiles).
+//   * The prefix is cut into splits of `kc` keys; the last split of a sequence
+//     also takes the tree keys (in 64-key tiles, tile t uses mask word t).
+//     Splits of one sequence write (m, l, O) partials that a second kernel
+//     merges in split order, so results are bitwise reproducible.
+//   * Workgroup ids are remapped so that the query blocks sharing one key
+//     split run on the same XCD (hardware dispatches ids round-robin over the
+//     8 XCDs) and share its L2.
+//
+// bf16 path, per 64-key tile: the workgroup copies K and V rows (coalesced
+// 16-byte loads, prefetched one tile ahead in registers) into LDS, rows
+// padded against bank conflicts.  Each wave computes S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims read as one 16-byte LDS
+// word per lane, B = the wave's Q fragment kept in registers), so a lane ends
+// up holding 8 scores of one query row.  Online softmax runs in fp32 in the
+// base-2 domain.  Then O^T += V^T P^T: P (rounded to bf16) is already in the B
+// operand layout, and V^T comes from LDS with ds_read_b64_tr_b16, which hands
+// lane (d, group) the values of 4 keys at dimension d.
+//
+// fp32 path: the same split structure with VALU arithmetic (one lane per key
+// for Q K^T, one lane per dimension for P V).
+#include "svt_internal.h"
+
+namespace svt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+constexpr int KT = 64;  // keys per LDS tile
+
+struct AttnDev {
+  const void* q;
+  const void* kcache;
+  const void* vcache;
+  const void* ktree;
+  const void* vtree;
+  const uint64_t* mask;
+  const int32_t* len;
+  const int32_t* lmax;
+  const int32_t* status;
+  void* out;
+  int32_t* seq_status;
+  float* ws_o;   // [B][Hkv][ns][R][D]
+  float* ws_ml;  // [B][Hkv][ns][R][2]
+  int64_t cap;
+  int B, T, Hq, Hkv, G, R, W;
+  int lmax_bound, kc, ns, nqb, qb_rows, nwg;
+  float scale_log2;
+};
+
+// Decoded workgroup coordinates and the sequence's key ranges.
+struct WgCtx {
+  int b, g, split, qb;
+  int code;        // SVT_OK or why the sequence is skipped
+  int L, lmax;
+  int ns_b;        // splits this sequence uses
+  int k_beg, k_end;
+  int n_ptiles, n_ttiles;
+};
+
+__device__ __forceinline__ bool decode_wg(const AttnDev& a, WgCtx& c) {
+  // XCD-aware remap: hardware id w runs on XCD w % 8; give each XCD a
+  // contiguous range of logical ids (query block fastest).
+  const int per = (a.nwg + 7) / 8;
+  const int w = blockIdx.x;
+  const int logical = (w % 8) * per + (w / 8);
+  if (logical >= a.nwg) return false;
+  c.qb = logical % a.nqb;
+  int rest = logical / a.nqb;
+  c.split = rest % a.ns;
+  rest /= a.ns;
+  c.g = rest % a.Hkv;
+  c.b = rest / a.Hkv;
+  c.lmax = *a.lmax;
+  c.L = a.len[c.b];
+  const int st = a.status ? a.status[c.b] : SVT_OK;
+  const bool len_ok = c.lmax >= 0 && c.lmax <= a.lmax_bound && c.L >= 0 && c.L <= c.lmax;
+  c.code = st != SVT_OK ? st : (len_ok ? SVT_OK : SVT_ERR_LENGTH);
+  c.ns_b = c.code == SVT_OK ? max(1, (c.L + a.kc - 1) / a.kc) : 1;
+  if (c.split >= c.ns_b) return false;
+  c.k_beg = c.split * a.kc;
+  c.k_end = c.code == SVT_OK ? min(c.L, c.k_beg + a.kc) : c.k_beg;
+  c.n_ptiles = c.k_end > c.k_beg ? (c.k_end - c.k_beg + KT - 1) / KT : 0;
+  c.n_ttiles = (c.split == c.ns_b - 1) ? (a.T + KT - 1) / KT : 0;
+  return true;
+}
+
+template <typename E>
+__device__ void write_zero_rows(const AttnDev& a, const WgCtx& c, int D) {
+  // Skipped sequence: split 0 writes zeros over the rows of its query block.
+  E* out = static_cast<E*>(a.out);
+  const int r0 = c.qb * a.qb_rows;
+  const int r1 = min(a.R, r0 + a.qb_rows);
+  for (int x = threadIdx.x; x < (r1 - r0) * D; x += blockDim.x) {
+    const int r = r0 + x / D, d = x % D;
+    const int hl = r / a.T, i = r % a.T;
+    out[(((int64_t)c.b * a.T + i) * a.Hq + c.g * a.G + hl) * D + d] = E(0.0f);
+  }
+}
+
+__device__ __forceinline__ void write_seq_status(const AttnDev& a, const WgCtx& c) {
+  if (a.seq_status && c.split == 0 && c.qb == 0 && c.g == 0 && threadIdx.x == 0) a.seq_status[c.b] = c.code;
+}
+
+// --------------------------------------------------------------------------
+// bf16 MFMA kernel
+// --------------------------------------------------------------------------
+template <int D>
+struct Lds {
+  static constexpr int KSTRIDE = D * 2 + 16;  // bytes per K row
+  static constexpr int VSTRIDE = D * 2 + 32;  // bytes per V row
+  static constexpr int KBYTES = KT * KSTRIDE;
+  static constexpr int VBYTES = KT * VSTRIDE;
+  static constexpr int STAGE = KBYTES + VBYTES;
+};
+
+template <int D, int QW>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
+  constexpr int NKS = D / 32;        // 32-wide k steps over the head dim
+  constexpr int NDT = D / 16;        // 16-wide output dim tiles
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int NLD = KT * CPR / 256;  // chunks per thread per tile (K or V)
+  using L = Lds<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * L::STAGE];
+
+  WgCtx c;
+  if (!decode_wg(a, c)) return;
+  write_seq_status(a, c);
+  if (c.code != SVT_OK) {
+    if (c.split == 0) write_zero_rows<__bf16>(a, c, D);
+    return;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n16 = lane & 15;   // row/col inside a 16x16 tile
+  const int grp = lane >> 4;   // lane group 0..3
+  const int nwk = (a.qb_rows == 32) ? 2 : 1;  // 2 waves per row-set when the block has 2 tiles
+  const int wq = wave / nwk, wk = wave % nwk;
+
+  const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.kcache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.vcache);
+  const uint16_t* __restrict__ ktr = static_cast<const uint16_t*>(a.ktree);
+  const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
+  const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query row n16 of
+  // each of its tiles, dims ks*32 + 8*grp .. +7.
+  bf16x8 qf[QW][NKS];
+  int row_node[QW];      // node index of this lane's query row, -1 if padding
+  int row_head[QW];
+#pragma unroll
+  for (int t = 0; t < QW; ++t) {
+    const int r = c.qb * a.qb_rows + (wq * QW + t) * 16 + n16;
+    const bool ok = r < a.R;
+    row_node[t] = ok ? r % a.T : -1;
+    row_head[t] = ok ? c.g * a.G + r / a.T : 0;
+    const uint16_t* qrow = q + (((int64_t)c.b * a.T + (ok ? row_node[t] : 0)) * a.Hq + row_head[t]) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ok) {
+        qf[t][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[t][ks][e] = (__bf16)0.0f;
+      }
+    }
+  }
+  // Is any row of each tile real?  (wave-uniform)
+  bool tile_live[QW];
+#pragma unroll
+  for (int t = 0; t < QW; ++t) tile_live[t] = c.qb * a.qb_rows + (wq * QW + t) * 16 < a.R;
+
+  f32x4 o[QW][NDT];
+  float m_run[QW], l_run[QW];
+#pragma unroll
+  for (int t = 0; t < QW; ++t) {
+    m_run[t] = kNegInf;
+    l_run[t] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int n_tiles = c.n_ptiles + c.n_ttiles;
+  const int pad = c.lmax - c.L;
+
+  // ---- tile loader: global -> registers -> LDS
+  uint4 stg[2 * NLD];
+  auto tile_rows = [&](int t, const uint16_t*& kb, const uint16_t*& vb, int& nvalid) {
+    if (t < c.n_ptiles) {
+      const int k0 = c.k_beg + t * KT;
+      const int64_t col = (int64_t)pad + k0;
+      kb = kc + (bg * a.cap + col) * D;
+      vb = vc + (bg * a.cap + col) * D;
+      nvalid = min(KT, c.k_end - k0);
+    } else {
+      const int j0 = (t - c.n_ptiles) * KT;
+      kb = ktr + (bg * a.T + j0) * D;
+      vb = vtr + (bg * a.T + j0) * D;
+      nvalid = min(KT, a.T - j0);
+    }
+  };
+  auto load_tile = [&](int t) {
+    const uint16_t *kb, *vb;
+    int nvalid;
+    tile_rows(t, kb, vb, nvalid);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int x = tid + 256 * j;
+      const int row = x / CPR, ch = x % CPR;
+      if (row < nvalid) {
+        stg[j] = *reinterpret_cast<const uint4*>(kb + (int64_t)row * D + ch * 8);
+        stg[NLD + j] = *reinterpret_cast<const uint4*>(vb + (int64_t)row * D + ch * 8);
+      } else {
+        stg[j] = make_uint4(0, 0, 0, 0);
+        stg[NLD + j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* kl = lds + buf * L::STAGE;
+    unsigned char* vl = kl + L::KBYTES;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int x = tid + 256 * j;
+      const int row = x / CPR, ch = x % CPR;
+      *reinterpret_cast<uint4*>(kl + row * L::KSTRIDE + ch * 16) = stg[j];
+      *reinterpret_cast<uint4*>(vl + row * L::VSTRIDE + ch * 16) = stg[NLD + j];
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    const bool tree_tile = t >= c.n_ptiles;
+    int nvalid;
+    {
+      const uint16_t *kb_, *vb_;
+      tile_rows(t, kb_, vb_, nvalid);
+    }
+    uint64_t mword[QW];
+    if (tree_tile) {
+      const int tt = t - c.n_ptiles;
+#pragma unroll
+      for (int qt = 0; qt < QW; ++qt)
+        mword[qt] = row_node[qt] >= 0 ? a.mask[((int64_t)c.b * a.T + row_node[qt]) * a.W + tt] : 0ull;
+    }
+    const unsigned char* kl = lds + buf * L::STAGE;
+    const unsigned char* vl = kl + L::KBYTES;
+
+    for (int half = 0; half < 2; ++half) {
+      if (nwk == 2 && half != wk) continue;
+      const int kb0 = half * 32;
+      if (kb0 >= nvalid) continue;  // wave-uniform: nothing valid in this half
+
+      // K fragments: A operand rows = keys kb0 + 16u + n16, dims ks*32 + 8*grp
+      bf16x8 kf[2][NKS];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          kf[u][ks] = *reinterpret_cast<const bf16x8*>(kl + (kb0 + 16 * u + n16) * L::KSTRIDE +
+                                                       (ks * 32 + grp * 8) * 2);
+      bf16x8 pf[QW];
+#pragma unroll
+      for (int qt = 0; qt < QW; ++qt) {
+        if (!tile_live[qt]) continue;
+        f32x4 s[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], s[u], 0, 0, 0);
+        }
+        // lane holds scores of query n16 for keys kb0 + 16u + 4*grp + e
+        float x[8];
+        float tmax = kNegInf;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kk = kb0 + 16 * u + 4 * grp + e;
+            bool ok = row_node[qt] >= 0 && kk < nvalid;
+            if (tree_tile) ok = ok && ((mword[qt] >> kk) & 1ull);
+            const float v = ok ? s[u][e] * a.scale_log2 : kNegInf;
+            x[u * 4 + e] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run[qt], tmax);
+        const float m_use = m_new == kNegInf ? 0.0f : m_new;
+        const float alpha = exp2f(m_run[qt] - m_use);
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2f(x[e] - m_use);
+          psum += p;
+          pf[qt][e] = (__bf16)p;
+        }
+        l_run[qt] = l_run[qt] * alpha + psum;
+        m_run[qt] = m_new;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+      }
+      // V^T fragments via transposing LDS reads; lane (lambda) addresses key
+      // kb0 + 4*(lambda/16) + (lambda%16)/4 (+16), dims dt*16 + 4*(lambda%4).
+      const int vkey = kb0 + 4 * grp + (n16 >> 2);
+      const int vdim = 4 * (lane & 3);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const lds_s16x4* p1 = (const lds_s16x4*)(vl + vkey * L::VSTRIDE + (dt * 16 + vdim) * 2);
+        const lds_s16x4* p2 = (const lds_s16x4*)(vl + (vkey + 16) * L::VSTRIDE + (dt * 16 + vdim) * 2);
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+        const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p2);
+        const s16x8 v12 = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, v12);
+#pragma unroll
+        for (int qt = 0; qt < QW; ++qt) {
+          if (!tile_live[qt]) continue;
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
+        }
+      }
+    }
+
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- two waves that split key tiles merge their states through LDS
+  float* xo = reinterpret_cast<float*>(lds);
+  if (nwk == 2) {
+    // per wave pair: QW*NDT*4 floats per lane + m + l
+    constexpr int PER_LANE = QW * NDT * 4 + 2 * QW;
+    float* slot = xo + (wq * 64 + lane) * PER_LANE;
+    if (wk == 1) {
+      int k = 0;
+#pragma unroll
+      for (int qt = 0; qt < QW; ++qt) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) slot[k++] = o[qt][dt][e];
+        slot[k++] = m_run[qt];
+        slot[k++] = l_run[qt];
+      }
+    }
+    __syncthreads();
+    if (wk == 1) return;
+    int k = 0;
+#pragma unroll
+    for (int qt = 0; qt < QW; ++qt) {
+      f32x4 o1[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o1[dt][e] = slot[k++];
+      const float m1 = slot[k++];
+      const float l1 = slot[k++];
+      const float mm = fmaxf(m_run[qt], m1);
+      const float mu = mm == kNegInf ? 0.0f : mm;
+      const float a0 = exp2f(m_run[qt] - mu), a1 = exp2f(m1 - mu);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = o[qt][dt] * a0 + o1[dt] * a1;
+      l_run[qt] = l_run[qt] * a0 + l1 * a1;
+      m_run[qt] = mm;
+    }
+  }
+
+  // ---- epilogue: lane holds O^T[d = dt*16 + 4*grp + e][query n16]
+  const bool direct = c.ns_b == 1;
+#pragma unroll
+  for (int qt = 0; qt < QW; ++qt) {
+    if (!tile_live[qt]) continue;
+    float lt = l_run[qt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (row_node[qt] < 0) continue;
+    const int r = c.qb * a.qb_rows + (wq * QW + qt) * 16 + n16;
+    if (direct) {
+      const float inv = 1.0f / lt;
+      __bf16* orow = static_cast<__bf16*>(a.out) +
+                     (((int64_t)c.b * a.T + row_node[qt]) * a.Hq + row_head[qt]) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[qt][dt][e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * grp) = v;
+      }
+    } else {
+      const int64_t pr = ((bg * a.ns + c.split) * a.R + r);
+      float* po = a.ws_o + pr * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[qt][dt];
+      if (grp == 0) {
+        a.ws_ml[pr * 2 + 0] = m_run[qt];
+        a.ws_ml[pr * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// fp32 VALU kernel: 64 query rows per workgroup, 16 per wave.
+// --------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
+  constexpr int DPL = D / 64;  // dims per lane
+  constexpr int KS = D + 1;    // padded K row (floats) against bank conflicts
+  __shared__ float qs[64 * D];
+  __shared__ float ks[KT * KS];
+  __shared__ float vs[KT * D];
+  __shared__ float ps[4][KT];
+
+  WgCtx c;
+  if (!decode_wg(a, c)) return;
+  write_seq_status(a, c);
+  if (c.code != SVT_OK) {
+    if (c.split == 0) write_zero_rows<float>(a, c, D);
+    return;
+  }
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* __restrict__ q = static_cast<const float*>(a.q);
+  const float* __restrict__ kc = static_cast<const float*>(a.kcache);
+  const float* __restrict__ vc = static_cast<const float*>(a.vcache);
+  const float* __restrict__ ktr = static_cast<const float*>(a.ktree);
+  const float* __restrict__ vtr = static_cast<const float*>(a.vtree);
+  const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
+  const int r0 = c.qb * 64;
+
+  for (int x = tid; x < 64 * D; x += 256) {
+    const int rr = x / D, d = x % D, r = r0 + rr;
+    float v = 0.0f;
+    if (r < a.R) v = q[(((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D + d];
+    qs[x] = v;
+  }
+  float m_run[16], l_run[16], o[16][DPL];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    m_run[j] = kNegInf;
+    l_run[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[j][e] = 0.0f;
+  }
+  const int n_tiles = c.n_ptiles + c.n_ttiles;
+  const int pad = c.lmax - c.L;
+  for (int t = 0; t < n_tiles; ++t) {
+    const float *kb, *vb;
+    int nvalid;
+    const bool tree_tile = t >= c.n_ptiles;
+    if (!tree_tile) {
+      const int k0 = c.k_beg + t * KT;
+      kb = kc + (bg * a.cap + pad + k0) * D;
+      vb = vc + (bg * a.cap + pad + k0) * D;
+      nvalid = min(KT, c.k_end - k0);
+    } else {
+      const int j0 = (t - c.n_ptiles) * KT;
+      kb = ktr + (bg * a.T + j0) * D;
+      vb = vtr + (bg * a.T + j0) * D;
+      nvalid = min(KT, a.T - j0);
+    }
+    __syncthreads();
+    for (int x = tid; x < KT * D; x += 256) {
+      const int row = x / D, d = x % D;
+      const bool ok = row < nvalid;
+      ks[row * KS + d] = ok ? kb[(int64_t)row * D + d] : 0.0f;
+      vs[x] = ok ? vb[(int64_t)row * D + d] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j < 16; ++j) {
+      const int rr = wave * 16 + j, r = r0 + rr;
+      if (r >= a.R) break;  // wave-uniform
+      const int node = r % a.T;
+      bool ok = lane < nvalid;
+      if (tree_tile) {
+        const uint64_t mw = a.mask[((int64_t)c.b * a.T + node) * a.W + (t - c.n_ptiles)];
+        ok = ok && ((mw >> lane) & 1ull);
+      }
+      float s = 0.0f;
+      for (int d = 0; d < D; ++d) s += qs[rr * D + d] * ks[lane * KS + d];
+      const float x = ok ? s * a.scale_log2 : kNegInf;
+      float tmax = x;
+      for (int off = 32; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+      const float m_new = fmaxf(m_run[j], tmax);
+      const float m_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = exp2f(m_run[j] - m_use);
+      const float p = exp2f(x - m_use);
+      float psum = p;
+      for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off);
+      l_run[j] = l_run[j] * alpha + psum;
+      m_run[j] = m_new;
+      ps[wave][lane] = p;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        float acc = o[j][e] * alpha;
+        const int d = lane + 64 * e;
+        for (int k = 0; k < KT; ++k) acc += ps[wave][k] * vs[k * D + d];
+        o[j][e] = acc;
+      }
+    }
+  }
+  const bool direct = c.ns_b == 1;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = r0 + wave * 16 + j;
+    if (r >= a.R) break;
+    if (direct) {
+      float* orow = static_cast<float*>(a.out) + (((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = o[j][e] / l_run[j];
+    } else {
+      const int64_t pr = (bg * a.ns + c.split) * a.R + r;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) a.ws_o[pr * D + lane + 64 * e] = o[j][e];
+      if (lane == 0) {
+        a.ws_ml[pr * 2 + 0] = m_run[j];
+        a.ws_ml[pr * 2 + 1] = l_run[j];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Split combine: one wave per query row, splits merged in index order.
+// --------------------------------------------------------------------------
+template <int D, typename E>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
+  constexpr int DPL = D / 64;
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= a.R) return;
+  const int lmax = *a.lmax;
+  const int L = a.len[b];
+  const int st = a.status ? a.status[b] : SVT_OK;
+  if (st != SVT_OK || !(lmax >= 0 && lmax <= a.lmax_bound && L >= 0 && L <= lmax)) return;
+  const int ns_b = max(1, (L + a.kc - 1) / a.kc);
+  if (ns_b <= 1) return;
+  const int64_t base = ((int64_t)b * a.Hkv + g) * a.ns;
+  float mx = kNegInf;
+  for (int s = 0; s < ns_b; ++s) mx = fmaxf(mx, a.ws_ml[((base + s) * a.R + r) * 2]);
+  const float mu = mx == kNegInf ? 0.0f : mx;
+  float lsum = 0.0f, acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
+  for (int s = 0; s < ns_b; ++s) {
+    const int64_t pr = (base + s) * a.R + r;
+    const float w = exp2f(a.ws_ml[pr * 2] - mu);
+    lsum += a.ws_ml[pr * 2 + 1] * w;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += a.ws_o[pr * D + lane + 64 * e] * w;
+  }
+  E* orow = static_cast<E*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
+  const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = E(acc[e] * inv);
+}
+
+// --------------------------------------------------------------------------
+// host side
+// --------------------------------------------------------------------------
+bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
+  if (!a || a->B < 0 || a->M < 0 || a->M >= SVT_MAX_T || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0 ||
+      (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16) || a->cap < 0 ||
+      a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap)
+    return false;
+  p->T = a->M + 1;
+  p->G = a->Hq / a->Hkv;
+  p->R = p->G * p->T;
+  p->nqt = (p->R + 15) / 16;
+  if (a->dtype == SVT_BF16) {
+    if (p->nqt <= 2) { p->nwk = 2; p->qw = 1; }
+    else if (p->nqt <= 4) { p->nwk = 1; p->qw = 1; }
+    else if (p->nqt <= 8) { p->nwk = 1; p->qw = 2; }
+    else if (p->nqt <= 12) { p->nwk = 1; p->qw = 3; }
+    else { p->nwk = 1; p->qw = 4; }
+    p->qb_rows = (4 / p->nwk) * p->qw * 16;
+  } else {
+    p->nwk = 1;
+    p->qw = 1;
+    p->qb_rows = 64;
+  }
+  p->nqb = (p->R + p->qb_rows - 1) / p->qb_rows;
+  // Prefix split size: enough workgroups to cover the chip several times over,
+  // fewer when the workgroups are heavy (their partials cost more).
+  const int64_t ptiles = ((int64_t)a->lmax_bound + KT - 1) / KT;
+  const int64_t units = ptiles * a->B * a->Hkv * p->nqb;
+  const int64_t target = (p->qw >= 4) ? 512 : 1024;
+  int64_t tiles_per_split = (units + target - 1) / (target > 0 ? target : 1);
+  if (tiles_per_split < 4) tiles_per_split = 4;
+  p->kc = (int)(tiles_per_split * KT);
+  p->ns = a->lmax_bound > 0 ? (int)((a->lmax_bound + p->kc - 1) / p->kc) : 1;
+  if (p->ns < 1) p->ns = 1;
+  p->ws_bytes = p->ns > 1 ? (size_t)a->B * a->Hkv * p->ns * p->R * (a->D + 2) * sizeof(float) : 0;
+  return true;
+}
+
+hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream_t s) {
+  AttnDev d;
+  d.q = a->q;
+  d.kcache = a->k_cache;
+  d.vcache = a->v_cache;
+  d.ktree = a->k_tree;
+  d.vtree = a->v_tree;
+  d.mask = a->mask;
+  d.len = a->len;
+  d.lmax = a->lmax;
+  d.status = a->status;
+  d.out = a->out;
+  d.seq_status = a->seq_status;
+  float* ws = static_cast<float*>(a->workspace);
+  const size_t n_o = p.ns > 1 ? (size_t)a->B * a->Hkv * p.ns * p.R * a->D : 0;
+  d.ws_o = ws;
+  d.ws_ml = ws ? ws + n_o : nullptr;
+  d.cap = a->cap;
+  d.B = a->B;
+  d.T = p.T;
+  d.Hq = a->Hq;
+  d.Hkv = a->Hkv;
+  d.G = p.G;
+  d.R = p.R;
+  d.W = (p.T + 63) / 64;
+  d.lmax_bound = a->lmax_bound;
+  d.kc = p.kc;
+  d.ns = p.ns;
+  d.nqb = p.nqb;
+  d.qb_rows = p.qb_rows;
+  const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
+  d.scale_log2 = scale * kLog2e;
+  const int64_t nwg = (int64_t)a->B * a->Hkv * p.ns * p.nqb;
+  if (nwg == 0) return hipSuccess;
+  if (nwg > 0x7FFFFFF0) return hipErrorInvalidValue;
+  d.nwg = (int)nwg;
+  const unsigned grid = (unsigned)(8 * ((nwg + 7) / 8));
+  const dim3 block(256);
+  if (a->dtype == SVT_BF16) {
+#define SVT_ATTN_BF16(DD, QQ) hipLaunchKernelGGL((attn_bf16_kernel<DD, QQ>), dim3(grid), block, 0, s, d)
+    if (a->D == 128) {
+      switch (p.qw) {
+        case 1: SVT_ATTN_BF16(128, 1); break;
+        case 2: SVT_ATTN_BF16(128, 2); break;
+        case 3: SVT_ATTN_BF16(128, 3); break;
+        default: SVT_ATTN_BF16(128, 4); break;
+      }
+    } else {
+      switch (p.qw) {
+        case 1: SVT_ATTN_BF16(64, 1); break;
+        case 2: SVT_ATTN_BF16(64, 2); break;
+        case 3: SVT_ATTN_BF16(64, 3); break;
+        default: SVT_ATTN_BF16(64, 4); break;
+      }
+    }
+#undef SVT_ATTN_BF16
+  } else {
+    if (a->D == 128) hipLaunchKernelGGL(attn_fp32_kernel<128>, dim3(grid), block, 0, s, d);
+    else hipLaunchKernelGGL(attn_fp32_kernel<64>, dim3(grid), block, 0, s, d);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.ns <= 1) return e;
+  const dim3 cgrid((p.R + 3) / 4, a->Hkv, a->B);
+  if (a->dtype == SVT_BF16) {
+    if (a->D == 128) hipLaunchKernelGGL((attn_combine_kernel<128, __bf16>), cgrid, block, 0, s, d);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, __bf16>), cgrid, block, 0, s, d);
+  } else {
+    if (a->D == 128) hipLaunchKernelGGL((attn_combine_kernel<128, float>), cgrid, block, 0, s, d);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, float>), cgrid, block, 0, s, d);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svt
