@@ -1,0 +1,312 @@
+"""Benchmark of one tree-verification round on one MI355X.
+
+A step is one full round over one batch of the B=32 ragged workload (GQA
+32/8 heads, head dim 128, prefix lengths uniform in [1024, 8192], M=32 draft
+nodes per tree, vocabulary 32000, 36 cache layers):
+    svt_build_mask -> svt_verify_attention for each of the 36 layers ->
+    svt_accept over the vocabulary -> svt_commit of all 36 layers.
+Inputs are resident in HBM before timing starts.  Each step starts from the
+same lengths (a device-to-device copy of 132 bytes restores len/lmax), so
+every timed step moves exactly the workload's bytes.
+
+Prints one JSON line.  `value` is verified tree nodes per second of the full
+step (B*M nodes per round).  Per-call durations come from HIP events recorded
+on the stream the library launches on; the `roofline` object is for the
+dominant call, `roofline_attention` for the attention call.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "tree-verify attn GB/s (% HBM peak) + verified tree nodes/s; commit µs/round"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="4", help="workload index or name (default: the B=32 ragged round)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes_attention(w, lens, T):
+    e = w.esize
+    q = w.B * T * w.Hq * w.D * e
+    kv = int(lens.sum()) * w.Hkv * w.D * e * 2
+    tree = w.B * w.Hkv * T * w.D * e * 2
+    mask = w.B * T * ((T + 63) // 64) * 8
+    return q + kv + tree + q + mask
+
+
+def flops_attention(w, lens, depth):
+    # 4 * Hq * D per (query, key) pair actually attended: prefix keys plus ancestors
+    T = w.T
+    pairs = int(lens.sum()) * T + int((depth + 1).sum())
+    return 4 * w.Hq * w.D * pairs
+
+
+def algorithmic_bytes_commit(w, lens, A, n_layers):
+    row = w.D * w.esize
+    lmax = int(lens.max())
+    new_len = lens + A
+    new_lmax = int(new_len.max())
+    moved = (lmax - lens) != (new_lmax - new_len)
+    kv = 0
+    for b in range(w.B):
+        if moved[b]:
+            kv += 2 * int(lens[b]) * row          # read + write of the shifted content
+        kv += 2 * int(A[b]) * row                 # gather: read branch row, write main row
+    kv *= n_layers * 2 * w.Hkv
+    tok = sum(2 * int(lens[b]) * 4 for b in range(w.B) if moved[b]) + 2 * int(A.sum()) * 4
+    pos = w.B * new_lmax * 4
+    return kv + tok + pos
+
+
+def algorithmic_bytes_accept(w):
+    return w.B * w.T * w.V * 4
+
+
+def cpu_baseline(w, parents, lens, logits, tokens, seed, budget_s):
+    """Time the oracle (single-threaded C, double precision) on a bounded
+    sample of the same workload and scale it to one full step."""
+    import oracle
+    from synth import gen
+    from synth import workloads as wl
+
+    t_all = time.perf_counter()
+    lmax = int(lens.max())
+    # mask + validate: whole batch
+    t0 = time.perf_counter()
+    _, st = oracle.validate(parents, w.M)
+    mk, dp = oracle.mask(parents, w.M, st)
+    t_mask = time.perf_counter() - t0
+    # argmax + accept: whole batch (the logits the GPU also read)
+    t0 = time.perf_counter()
+    am = oracle.argmax(logits)
+    al, path, _ = oracle.accept(am, tokens, parents, w.M, st)
+    t_accept = time.perf_counter() - t0
+    # attention: whole sequences of one layer, in a seeded order, until the
+    # sample (inputs included) has used about half the budget
+    order = np.argsort(gen.u64(gen.stream_key(seed, 991), w.B))
+    picked, t_attn_sample, keys_sample = [], 0.0, 0
+    t_part = time.perf_counter()
+    sub = wl.Workload(**{**w.__dict__, "B": 1})
+    for b in order:
+        if picked and time.perf_counter() - t_part > 0.5 * budget_s:
+            break
+        Lb = int(lens[b])
+        q, kc, vc, kt, vt = wl.attention_inputs(sub, np.array([Lb], np.int32), Lb, seed + 1000 + int(b),
+                                                poison=False)
+        f = lambda x: wl.as_f32(sub, x)
+        args = (f(q), f(kc), f(vc), f(kt), f(vt), mk[b:b + 1], np.array([Lb], np.int32), Lb)
+        t0 = time.perf_counter()
+        oracle.attention(*args)
+        t_attn_sample += time.perf_counter() - t0
+        keys_sample += Lb
+        picked.append(int(b))
+    t_attn_layer = t_attn_sample * float(lens.sum()) / max(keys_sample, 1)
+    # commit: one layer, one KV head (every layer, plane and head moves the
+    # same way); the bytes moved do not depend on their values
+    T = w.T
+    cap = lmax + T + 8
+    row_el = w.D * w.esize // 2
+    km = (np.arange(2 * w.B * cap * row_el, dtype=np.uint32) & 0xFFFF).astype(np.uint16)
+    km = km.reshape(1, 2, w.B, 1, cap, row_el)
+    kb = np.ones((1, 2, w.B, 1, T, row_el), np.uint16)
+    tm = np.zeros((w.B, cap), np.int32)
+    t0 = time.perf_counter()
+    oracle.commit(km, kb, w.M, tm, tokens, lens, lmax, path, al, st)
+    t_commit_slab = time.perf_counter() - t0
+    t_commit = t_commit_slab * w.layers * w.Hkv
+    step_s = t_mask + w.layers * t_attn_layer + t_accept + t_commit
+    return {
+        "value": w.B * w.M / step_s,
+        "unit": "verified tree nodes/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"oracle (1 thread, fp64) on the same workload: mask+accept for all {w.B} sequences; "
+                   f"one-layer attention for sequences {picked} ({keys_sample} of {int(lens.sum())} prefix "
+                   f"keys), scaled by keys and by {w.layers} layers; commit of one layer and one KV head, "
+                   f"scaled by {w.layers} layers x {w.Hkv} heads; {time.perf_counter() - t_all:.1f} s wall"),
+        "est_step_s": step_s,
+        "est_parts_s": {"mask": t_mask, "attention_per_layer": t_attn_layer, "accept": t_accept,
+                        "commit": t_commit},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(collectives and sharding are out of its scope); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import workloads as wl
+    from tree_masked_verification_parent_amd import svt
+    from tree_masked_verification_parent_amd.round import VerifyRound
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wkey = int(args.workload) if args.workload.isdigit() else args.workload
+    w = wl.workload(wkey)
+    dtype = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    seed = w.seed
+    parents = wl.trees(w, seed)
+    lens0 = wl.lengths(w, seed)
+    lmax0 = int(lens0.max())
+    logits, tokens, _ = wl.logits_and_drafts(w, parents, seed)
+    cap = lmax0 + w.T + 64
+    L = w.layers
+
+    r = VerifyRound(w.B, w.M, w.Hq, w.Hkv, w.D, w.V, cap, L, dtype, attn_layers=L)
+    dev = r.q.device
+    r.parents.copy_(torch.from_numpy(parents))
+    r.tree_tokens.copy_(torch.from_numpy(tokens))
+    r.logits.copy_(torch.from_numpy(logits))
+    gen_t = torch.Generator(device=dev)
+    gen_t.manual_seed(seed)
+    sig = w.qkv_sigma
+    for layer in range(L):  # seeded device-side normals for the large tensors
+        r.kv_main[layer].normal_(0.0, sig, generator=gen_t)
+        r.kv_branch[layer].normal_(0.0, sig, generator=gen_t)
+        r.q[layer].normal_(0.0, sig, generator=gen_t)
+    r.tokens_main.random_(0, w.V, generator=gen_t)
+    len0 = torch.from_numpy(lens0).to(dev)
+    lmax0_t = torch.tensor([lmax0], dtype=torch.int32, device=dev)
+    r.len.copy_(len0)
+    r.lmax.copy_(lmax0_t)
+    r.set_lmax_bound(lmax0)
+    torch.cuda.synchronize()
+
+    # first round (untimed): learn the accept lengths, which fix every later round
+    assert r.build_mask(svt.SVT_SYNC_CHECK) == 0
+    assert r.step() == 0
+    assert r.commit_status.item() == 0
+    A = r.accept_len.cpu().numpy().astype(np.int64) + 1
+    depth = r.depth.cpu().numpy()
+
+    stream = torch.cuda.current_stream()
+    n_ev = 4 + L
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)] for _ in range(args.steps)]
+
+    def one_step(ev=None):
+        r.len.copy_(len0)
+        r.lmax.copy_(lmax0_t)
+        if ev:
+            ev[0].record(stream)
+        rc = r.build_mask()
+        if ev:
+            ev[1].record(stream)
+        for layer in range(L):
+            rc = rc or r.attention(layer)
+            if ev:
+                ev[2 + layer].record(stream)
+        rc = rc or r.accept()
+        if ev:
+            ev[2 + L].record(stream)
+        rc = rc or r.commit()
+        if ev:
+            ev[3 + L].record(stream)
+        return rc
+
+    for _ in range(args.warmup):
+        assert one_step() == 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        rc = one_step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert rc == 0 and r.commit_status.item() == 0
+    assert np.array_equal(r.len.cpu().numpy(), lens0 + A)
+
+    def dur(i, j):
+        return float(np.mean([evs[k][i].elapsed_time(evs[k][j]) for k in range(args.steps)])) * 1e-3
+
+    t_mask = dur(0, 1)
+    t_attn_layers = [dur(1 + l, 2 + l) for l in range(L)]
+    t_attn = float(np.mean(t_attn_layers))
+    t_accept = dur(1 + L, 2 + L)
+    t_commit = dur(2 + L, 3 + L)
+    ms_per_step = elapsed / args.steps * 1e3
+
+    attn_bytes = algorithmic_bytes_attention(w, lens0, w.T)
+    attn_flops = flops_attention(w, lens0, depth)
+    commit_bytes = algorithmic_bytes_commit(w, lens0, A, L)
+    acc_bytes = algorithmic_bytes_accept(w)
+    attn_gbps = attn_bytes / t_attn / 1e9
+    commit_gbps = commit_bytes / t_commit / 1e9
+    totals = {"attention": t_attn * L, "commit": t_commit, "accept": t_accept, "mask": t_mask}
+    dominant = max(totals, key=totals.get)
+
+    def roof(kind):
+        if kind == "commit":
+            a = commit_gbps
+            return {"kernel": "commit_move_kernel (+ commit_finalize_kernel)", "bound": "hbm", "achieved": a,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS, "traffic": None,
+                    "bytes_per_launch": commit_bytes, "avg_launch_us": t_commit * 1e6}
+        if kind == "attention":
+            a = attn_gbps
+            return {"kernel": "attn_bf16_kernel (+ attn_combine_kernel)", "bound": "hbm", "achieved": a,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS, "traffic": None,
+                    "bytes_per_launch": attn_bytes, "avg_launch_us": t_attn * 1e6,
+                    "mfma_tflops": attn_flops / t_attn / 1e12,
+                    "mfma_frac": attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS}
+        if kind == "accept":
+            a = acc_bytes / t_accept / 1e9
+            return {"kernel": "argmax_partial_kernel (+ accept_kernel)", "bound": "hbm", "achieved": a,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS, "traffic": None,
+                    "bytes_per_launch": acc_bytes, "avg_launch_us": t_accept * 1e6}
+        return {"kernel": "build_mask_kernel", "bound": "latency", "achieved": None, "peak": None,
+                "unit": None, "frac": None, "traffic": None, "avg_launch_us": t_mask * 1e6}
+
+    out = {
+        "metric": METRIC,
+        "value": w.B * w.M / (ms_per_step * 1e-3),
+        "unit": "verified tree nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded trees, drafts, logits; device-seeded normal caches)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "M": w.M, "V": w.V,
+                   "prefix_len": [w.len_lo, w.len_hi], "layers": L, "sum_len": int(lens0.sum()),
+                   "mean_accept_len": float(np.mean(A - 1))},
+        "attn_GBps": attn_gbps,
+        "attn_frac_hbm": attn_gbps / HBM_PEAK_GBPS,
+        "attn_us_per_layer": t_attn * 1e6,
+        "commit_us_per_round": t_commit * 1e6,
+        "commit_GBps": commit_gbps,
+        "accept_us": t_accept * 1e6,
+        "mask_us": t_mask * 1e6,
+        "verified_nodes_per_s_one_layer": w.B * w.M / (t_mask + t_attn + t_accept),
+        "dominant": dominant,
+        "roofline": roof(dominant),
+        "roofline_attention": roof("attention"),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, parents, lens0, logits, tokens, seed, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,6 +48,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int KT = 64;  // keys per LDS tile
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold, base-2 units
 
 struct AttnDev {
   const void* q;
@@ -126,23 +127,76 @@ __device__ __forceinline__ void write_seq_status(const AttnDev& a, const WgCtx& 
 // --------------------------------------------------------------------------
 // bf16 MFMA kernel
 // --------------------------------------------------------------------------
+// One pipeline stage holds a K tile and a V tile, KT rows of D bf16 each, with
+// no padding.  Row r keeps its 16-byte chunk c at slot c ^ swz(r); the swizzles
+// spread the rows that one operand read touches over all 64 LDS banks (K: 16
+// rows x one chunk per ds_read_b128; V: 8 rows x two chunks x two halves per
+// 32 lanes of ds_read_b64_tr_b16).  Tiles are copied straight from HBM to LDS
+// with global_load_lds_dwordx4: one wave instruction fills 1 KB of LDS (64
+// lanes x 16 B, consecutive), so the swizzle is applied on the global side by
+// choosing which chunk each lane fetches.  No tile data passes through
+// registers, and kStages - 1 tiles are in flight while one is computed on.
 template <int D>
-struct Lds {
-  static constexpr int KSTRIDE = D * 2 + 16;  // bytes per K row
-  static constexpr int VSTRIDE = D * 2 + 32;  // bytes per V row
-  static constexpr int KBYTES = KT * KSTRIDE;
-  static constexpr int VBYTES = KT * VSTRIDE;
-  static constexpr int STAGE = KBYTES + VBYTES;
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  static constexpr int TILEB = KT * ROWB;     // one K or V tile
+  static constexpr int STAGEB = 2 * TILEB;
+  static constexpr int NINSTR = TILEB / 1024;  // 1 KB copy instructions per K or V tile
+  static constexpr int PER_WAVE = NINSTR / 4;  // per wave
+  static constexpr int LOADS = 2 * PER_WAVE;   // copy instructions per wave per stage
+  static constexpr int RPI = 1024 / ROWB;      // rows per copy instruction
+  __device__ static __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int swz_v(int r) { return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1); }
 };
+
+constexpr int kStages = 3;      // LDS ring: one tile computed, two in flight
+constexpr int kMaxQbRows = 256;  // query rows per workgroup
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte copy global -> LDS (global_load_lds_dwordx4).  The LDS address of
+// lane i is lds + 16 * i: `lds` must be the same for the whole wave.  Only the
+// device pass sees the builtin (the host pass drops kernels that use it).
+__device__ __forceinline__ void copy16_to_lds(const void* g, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+#endif
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that does not wait for outstanding global loads (the
+// copies of later tiles stay in flight); pending LDS reads are drained first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 lane-swap instructions.  With both operands equal to
+// x, the two results of a swap are x at lane l and at its partner, in some
+// order, so a symmetric combine of them gives the pairwise reduction.
+__device__ __forceinline__ float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int D, int QW>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
-  constexpr int NKS = D / 32;        // 32-wide k steps over the head dim
-  constexpr int NDT = D / 16;        // 16-wide output dim tiles
-  constexpr int CPR = D / 8;         // 16-byte chunks per row
-  constexpr int NLD = KT * CPR / 256;  // chunks per thread per tile (K or V)
-  using L = Lds<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * L::STAGE];
+  constexpr int NKS = D / 32;  // 32-wide k steps over the head dim
+  constexpr int NDT = D / 16;  // 16-wide output dim tiles
+  using TL = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * TL::STAGEB];
+  __shared__ uint64_t maskw[kMaxQbRows * 4];
 
   WgCtx c;
   if (!decode_wg(a, c)) return;
@@ -153,11 +207,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
   }
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave branches scalar
   const int lane = tid & 63;
-  const int n16 = lane & 15;   // row/col inside a 16x16 tile
-  const int grp = lane >> 4;   // lane group 0..3
-  const int nwk = (a.qb_rows == 32) ? 2 : 1;  // 2 waves per row-set when the block has 2 tiles
+  const int n16 = lane & 15;  // row/col inside a 16x16 tile
+  const int grp = lane >> 4;  // lane group 0..3
+  const int nwk = (a.qb_rows == 32) ? 2 : 1;  // 2 waves share the rows when the block has 2 tiles
   const int wq = wave / nwk, wk = wave % nwk;
 
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
@@ -166,15 +220,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
   const uint16_t* __restrict__ ktr = static_cast<const uint16_t*>(a.ktree);
   const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
   const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
+  const int r0 = c.qb * a.qb_rows;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query row n16 of
   // each of its tiles, dims ks*32 + 8*grp .. +7.
   bf16x8 qf[QW][NKS];
-  int row_node[QW];      // node index of this lane's query row, -1 if padding
+  int row_node[QW];  // node index of this lane's query row, -1 if padding
   int row_head[QW];
 #pragma unroll
   for (int t = 0; t < QW; ++t) {
-    const int r = c.qb * a.qb_rows + (wq * QW + t) * 16 + n16;
+    const int r = r0 + (wq * QW + t) * 16 + n16;
     const bool ok = r < a.R;
     row_node[t] = ok ? r % a.T : -1;
     row_head[t] = ok ? c.g * a.G + r / a.T : 0;
@@ -189,16 +244,28 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
       }
     }
   }
-  // Is any row of each tile real?  (wave-uniform)
-  bool tile_live[QW];
+  bool tile_live[QW];  // does the tile hold any real row?  (wave-uniform)
 #pragma unroll
-  for (int t = 0; t < QW; ++t) tile_live[t] = c.qb * a.qb_rows + (wq * QW + t) * 16 < a.R;
+  for (int t = 0; t < QW; ++t) tile_live[t] = r0 + (wq * QW + t) * 16 < a.R;
 
+  // Ancestor-mask words of the block's rows, for the tree tiles.
+  if (c.n_ttiles > 0) {
+    for (int x = tid; x < a.qb_rows * a.W; x += 256) {
+      const int rl = x / a.W, w = x % a.W, r = r0 + rl;
+      maskw[rl * 4 + w] = r < a.R ? a.mask[((int64_t)c.b * a.T + r % a.T) * a.W + w] : 0ull;
+    }
+  }
+  __syncthreads();
+
+  // Online softmax state per query row.  m_ref is the reference the
+  // accumulators are scaled to; it is moved (and O, l rescaled) only when the
+  // running maximum exceeds it by more than kRescale (base-2 units), which is
+  // rare after the first tiles.  The result O / l does not depend on m_ref.
   f32x4 o[QW][NDT];
-  float m_run[QW], l_run[QW];
+  float m_ref[QW], l_run[QW];
 #pragma unroll
   for (int t = 0; t < QW; ++t) {
-    m_run[t] = kNegInf;
+    m_ref[t] = kNegInf;
     l_run[t] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -207,8 +274,6 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
   const int n_tiles = c.n_ptiles + c.n_ttiles;
   const int pad = c.lmax - c.L;
 
-  // ---- tile loader: global -> registers -> LDS
-  uint4 stg[2 * NLD];
   auto tile_rows = [&](int t, const uint16_t*& kb, const uint16_t*& vb, int& nvalid) {
     if (t < c.n_ptiles) {
       const int k0 = c.k_beg + t * KT;
@@ -223,44 +288,35 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
       nvalid = min(KT, a.T - j0);
     }
   };
-  auto load_tile = [&](int t) {
+  // Copy tile t into stage `st` (every wave issues TL::LOADS instructions).
+  // Rows past the valid ones repeat the last valid row; they are masked out.
+  auto issue_tile = [&](int t, int st) {
     const uint16_t *kb, *vb;
     int nvalid;
     tile_rows(t, kb, vb, nvalid);
+    unsigned char* kl = lds + st * TL::STAGEB;
+    unsigned char* vl = kl + TL::TILEB;
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int x = tid + 256 * j;
-      const int row = x / CPR, ch = x % CPR;
-      if (row < nvalid) {
-        stg[j] = *reinterpret_cast<const uint4*>(kb + (int64_t)row * D + ch * 8);
-        stg[NLD + j] = *reinterpret_cast<const uint4*>(vb + (int64_t)row * D + ch * 8);
-      } else {
-        stg[j] = make_uint4(0, 0, 0, 0);
-        stg[NLD + j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* kl = lds + buf * L::STAGE;
-    unsigned char* vl = kl + L::KBYTES;
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int x = tid + 256 * j;
-      const int row = x / CPR, ch = x % CPR;
-      *reinterpret_cast<uint4*>(kl + row * L::KSTRIDE + ch * 16) = stg[j];
-      *reinterpret_cast<uint4*>(vl + row * L::VSTRIDE + ch * 16) = stg[NLD + j];
+    for (int j = 0; j < TL::PER_WAVE; ++j) {
+      const int ins = wave + 4 * j;
+      const int row = ins * TL::RPI + lane / TL::CPR;
+      const int slot = lane % TL::CPR;
+      const int64_t src = (int64_t)min(row, nvalid - 1) * D;
+      copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
+      copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < n_tiles) issue_tile(st, st);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    // tile t has landed once at most the copies of later tiles are pending
+    if (t + 1 < n_tiles) wait_vmcnt<TL::LOADS>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1, (t + kStages - 1) % kStages);
 
     const bool tree_tile = t >= c.n_ptiles;
     int nvalid;
@@ -268,80 +324,91 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
       const uint16_t *kb_, *vb_;
       tile_rows(t, kb_, vb_, nvalid);
     }
-    uint64_t mword[QW];
-    if (tree_tile) {
-      const int tt = t - c.n_ptiles;
+    // Valid-key bits of this tile for each of the lane's query rows: the first
+    // nvalid keys, and for tree tiles only the ancestors.
+    const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+    uint64_t vbits[QW];
 #pragma unroll
-      for (int qt = 0; qt < QW; ++qt)
-        mword[qt] = row_node[qt] >= 0 ? a.mask[((int64_t)c.b * a.T + row_node[qt]) * a.W + tt] : 0ull;
+    for (int qt = 0; qt < QW; ++qt) {
+      uint64_t v = row_node[qt] >= 0 ? head_bits : 0ull;
+      if (tree_tile) v &= maskw[((wq * QW + qt) * 16 + n16) * 4 + (t - c.n_ptiles)];
+      vbits[qt] = v;
     }
-    const unsigned char* kl = lds + buf * L::STAGE;
-    const unsigned char* vl = kl + L::KBYTES;
+    const unsigned char* kl = lds + (t % kStages) * TL::STAGEB;
+    const unsigned char* vl = kl + TL::TILEB;
 
+#pragma unroll 1
     for (int half = 0; half < 2; ++half) {
       if (nwk == 2 && half != wk) continue;
       const int kb0 = half * 32;
       if (kb0 >= nvalid) continue;  // wave-uniform: nothing valid in this half
 
-      // K fragments: A operand rows = keys kb0 + 16u + n16, dims ks*32 + 8*grp
-      bf16x8 kf[2][NKS];
+      // S^T = K Q^T: A operand rows = keys kb0 + 16u + n16, dims ks*32 + 8*grp
+      f32x4 s[QW][2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+        const int kr = kb0 + 16 * u + n16;
+        bf16x8 kf[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          kf[u][ks] = *reinterpret_cast<const bf16x8*>(kl + (kb0 + 16 * u + n16) * L::KSTRIDE +
-                                                       (ks * 32 + grp * 8) * 2);
+          kf[ks] = *reinterpret_cast<const bf16x8*>(kl + kr * TL::ROWB + 16 * ((ks * 4 + grp) ^ TL::swz_k(kr)));
+#pragma unroll
+        for (int qt = 0; qt < QW; ++qt) {
+          if (!tile_live[qt]) continue;
+          s[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            s[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[qt][ks], s[qt][u], 0, 0, 0);
+        }
+      }
       bf16x8 pf[QW];
 #pragma unroll
       for (int qt = 0; qt < QW; ++qt) {
         if (!tile_live[qt]) continue;
-        f32x4 s[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], s[u], 0, 0, 0);
-        }
         // lane holds scores of query n16 for keys kb0 + 16u + 4*grp + e
+        const uint32_t bits = (uint32_t)(vbits[qt] >> (kb0 + 4 * grp));
         float x[8];
         float tmax = kNegInf;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int kk = kb0 + 16 * u + 4 * grp + e;
-            bool ok = row_node[qt] >= 0 && kk < nvalid;
-            if (tree_tile) ok = ok && ((mword[qt] >> kk) & 1ull);
-            const float v = ok ? s[u][e] * a.scale_log2 : kNegInf;
+            const bool ok = (bits >> (16 * u + e)) & 1u;
+            const float v = ok ? s[qt][u][e] * a.scale_log2 : kNegInf;
             x[u * 4 + e] = v;
             tmax = fmaxf(tmax, v);
           }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run[qt], tmax);
-        const float m_use = m_new == kNegInf ? 0.0f : m_new;
-        const float alpha = exp2f(m_run[qt] - m_use);
+        tmax = group_max(tmax);
+        const float m_cand = fmaxf(m_ref[qt], tmax);
+        if (__any(m_cand > m_ref[qt] + kRescale)) {  // wave-uniform, rare
+          const float alpha = m_cand == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_cand);
+          l_run[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+          m_ref[qt] = m_cand;
+        }
+        const float m_eff = m_ref[qt] == kNegInf ? 0.0f : m_ref[qt];
         float psum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(x[e] - m_use);
+          const float p = __builtin_amdgcn_exp2f(x[e] - m_eff);
           psum += p;
           pf[qt][e] = (__bf16)p;
         }
-        l_run[qt] = l_run[qt] * alpha + psum;
-        m_run[qt] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+        l_run[qt] += psum;
       }
-      // V^T fragments via transposing LDS reads; lane (lambda) addresses key
-      // kb0 + 4*(lambda/16) + (lambda%16)/4 (+16), dims dt*16 + 4*(lambda%4).
-      const int vkey = kb0 + 4 * grp + (n16 >> 2);
-      const int vdim = 4 * (lane & 3);
+      // O^T += V^T P^T.  V^T fragments come from transposing LDS reads: lane
+      // (lambda) addresses key kb0 + 4*(lambda/16) + (lambda%16)/4 (+16),
+      // dims dt*16 + 4*(lambda%4).
+      const int vk1 = kb0 + 4 * grp + (n16 >> 2);
+      const int vk2 = vk1 + 16;
+      const int q4 = lane & 3;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const lds_s16x4* p1 = (const lds_s16x4*)(vl + vkey * L::VSTRIDE + (dt * 16 + vdim) * 2);
-        const lds_s16x4* p2 = (const lds_s16x4*)(vl + (vkey + 16) * L::VSTRIDE + (dt * 16 + vdim) * 2);
+        const int ch = 2 * dt + (q4 >> 1);
+        const int hb = 8 * (q4 & 1);
+        const unsigned char* p1 = vl + vk1 * TL::ROWB + 16 * (ch ^ TL::swz_v(vk1)) + hb;
+        const unsigned char* p2 = vl + vk2 * TL::ROWB + 16 * (ch ^ TL::swz_v(vk2)) + hb;
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
         const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p2);
         const s16x8 v12 = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -353,15 +420,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
         }
       }
     }
-
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
   }
+  lds_barrier();  // every wave is done with the stage buffers
 
   // ---- two waves that split key tiles merge their states through LDS
   float* xo = reinterpret_cast<float*>(lds);
   if (nwk == 2) {
-    // per wave pair: QW*NDT*4 floats per lane + m + l
     constexpr int PER_LANE = QW * NDT * 4 + 2 * QW;
     float* slot = xo + (wq * 64 + lane) * PER_LANE;
     if (wk == 1) {
@@ -372,7 +436,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) slot[k++] = o[qt][dt][e];
-        slot[k++] = m_run[qt];
+        slot[k++] = m_ref[qt];
         slot[k++] = l_run[qt];
       }
     }
@@ -388,13 +452,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
         for (int e = 0; e < 4; ++e) o1[dt][e] = slot[k++];
       const float m1 = slot[k++];
       const float l1 = slot[k++];
-      const float mm = fmaxf(m_run[qt], m1);
-      const float mu = mm == kNegInf ? 0.0f : mm;
-      const float a0 = exp2f(m_run[qt] - mu), a1 = exp2f(m1 - mu);
+      const float mm = fmaxf(m_ref[qt], m1);
+      const float a0 = mm == kNegInf ? 1.0f : exp2f(m_ref[qt] - mm);
+      const float a1 = mm == kNegInf ? 1.0f : exp2f(m1 - mm);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = o[qt][dt] * a0 + o1[dt] * a1;
       l_run[qt] = l_run[qt] * a0 + l1 * a1;
-      m_run[qt] = mm;
+      m_ref[qt] = mm;
     }
   }
 
@@ -403,15 +467,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 #pragma unroll
   for (int qt = 0; qt < QW; ++qt) {
     if (!tile_live[qt]) continue;
-    float lt = l_run[qt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = group_sum(l_run[qt]);
     if (row_node[qt] < 0) continue;
-    const int r = c.qb * a.qb_rows + (wq * QW + qt) * 16 + n16;
+    const int r = r0 + (wq * QW + qt) * 16 + n16;
     if (direct) {
       const float inv = 1.0f / lt;
-      __bf16* orow = static_cast<__bf16*>(a.out) +
-                     (((int64_t)c.b * a.T + row_node[qt]) * a.Hq + row_head[qt]) * D;
+      __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)c.b * a.T + row_node[qt]) * a.Hq + row_head[qt]) * D;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -426,7 +487,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[qt][dt];
       if (grp == 0) {
-        a.ws_ml[pr * 2 + 0] = m_run[qt];
+        a.ws_ml[pr * 2 + 0] = m_ref[qt];
         a.ws_ml[pr * 2 + 1] = lt;
       }
     }
