@@ -35,6 +35,8 @@
 //
 // fp32 path: the same split structure with VALU arithmetic (one lane per key
 // for Q K^T, one lane per dimension for P V).
+#include <type_traits>
+
 #include "svt_internal.h"
 
 namespace svt {
@@ -154,13 +156,16 @@ constexpr int kStages = 3;      // LDS ring: one tile computed, two in flight
 constexpr int kMaxQbRows = 256;  // query rows per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte copy global -> LDS (global_load_lds_dwordx4).  The LDS address of
-// lane i is lds + 16 * i: `lds` must be the same for the whole wave.  Only the
-// device pass sees the builtin (the host pass drops kernels that use it).
+// 16-byte copy global -> LDS (global_load_lds_dwordx4): lane i's 16 bytes land
+// at LDS address lds + 16 * i, with `lds` the same for the whole wave (it goes
+// to M0).  Issued as inline assembly on purpose: the compiler would otherwise
+// track these copies and wait for all of them (vmcnt(0)) before every use of
+// LDS data, which serialises the prefetch with the compute.  Completion is
+// tracked by hand with wait_vmcnt<N>() before the workgroup barrier.  M0 is
+// not used for anything else in the kernels of this file.
 __device__ __forceinline__ void copy16_to_lds(const void* g, unsigned char* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
-#endif
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_void*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory operations are pending.
@@ -247,6 +252,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
   bool tile_live[QW];  // does the tile hold any real row?  (wave-uniform)
 #pragma unroll
   for (int t = 0; t < QW; ++t) tile_live[t] = r0 + (wq * QW + t) * 16 < a.R;
+  // Waves with a real row compute all QW tiles (padding rows have Q = 0 and
+  // are never stored), so the MFMA chains need no per-tile branches.
+  const bool wave_live = __builtin_amdgcn_readfirstlane(tile_live[0] ? 1 : 0) != 0;
 
   // Ancestor-mask words of the block's rows, for the tree tiles.
   if (c.n_ttiles > 0) {
@@ -257,19 +265,41 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
   }
   __syncthreads();
 
-  // Online softmax state per query row.  m_ref is the reference the
-  // accumulators are scaled to; it is moved (and O, l rescaled) only when the
-  // running maximum exceeds it by more than kRescale (base-2 units), which is
-  // rare after the first tiles.  The result O / l does not depend on m_ref.
+  // Online softmax state per query row, in base-2 units of scale * q.k.
+  // m_ref is the reference the accumulators are scaled to; it moves (and O,
+  // l are rescaled) only when a score exceeds it by more than kRescale, which
+  // happens in the first tiles and then rarely.  O / l does not depend on it.
+  // Padding rows (Q = 0, so every score is exactly 0) start at m_ref = 0 and
+  // never trigger a rescale; their accumulators are never stored.
+  // l is accumulated by the matrix cores: one extra MFMA per 32 keys with an
+  // all-ones A operand sums the bf16 P exactly as the P V product uses it, and
+  // leaves the row sum in every element of the lane's accumulator.
   f32x4 o[QW][NDT];
-  float m_ref[QW], l_run[QW];
+  f32x4 lacc[QW];
+  float m_ref[QW];
 #pragma unroll
   for (int t = 0; t < QW; ++t) {
-    m_ref[t] = kNegInf;
-    l_run[t] = 0.0f;
+    m_ref[t] = row_node[t] >= 0 ? kNegInf : 0.0f;
+    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const float sc = a.scale_log2;
+
+  // Lane-constant LDS byte offsets.  Sub-tiles start at multiples of 16 keys
+  // (K) and 32 keys (V), so every swizzle depends on the lane alone.
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = n16 * TL::ROWB + 16 * ((ks * 4 + grp) ^ TL::swz_k(n16));
+  const int vrow = 4 * grp + (n16 >> 2);  // + kb0, and + 16 for the second read
+  const int q4 = lane & 3;
+  int voff[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+    voff[dt] = vrow * TL::ROWB + 16 * ((2 * dt + (q4 >> 1)) ^ TL::swz_v(vrow)) + 8 * (q4 & 1);
 
   const int n_tiles = c.n_ptiles + c.n_ttiles;
   const int pad = c.lmax - c.L;
@@ -307,6 +337,81 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
     }
   };
 
+  // One 32-key half of the current tile.  MASKED selects the path with
+  // per-key validity bits (ragged tail, tree tiles); full prefix halves skip it.
+  auto process_half = [&](auto masked_c, const unsigned char* kl, const unsigned char* vl, int kb0,
+                          const uint64_t* vbits) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    // S^T = K Q^T: A operand rows = keys kb0 + 16u + n16, dims ks*32 + 8*grp.
+    // All QW x 2 accumulation chains are advanced together so that
+    // consecutive MFMAs are independent.
+    const unsigned char* kh = kl + kb0 * TL::ROWB;
+    bf16x8 kf[2][NKS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        kf[u][ks] = *reinterpret_cast<const bf16x8*>(kh + 16 * u * TL::ROWB + koff[ks]);
+    f32x4 s[QW][2];
+#pragma unroll
+    for (int qt = 0; qt < QW; ++qt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) s[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int qt = 0; qt < QW; ++qt)
+          s[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], s[qt][u], 0, 0, 0);
+    bf16x8 pf[QW];
+#pragma unroll
+    for (int qt = 0; qt < QW; ++qt) {
+      // lane holds raw scores of query n16 for keys kb0 + 16u + 4*grp + e
+      float x[8];
+      uint32_t bits = 0;
+      if constexpr (MASKED) bits = (uint32_t)(vbits[qt] >> (kb0 + 4 * grp));
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = s[qt][u][e];
+          if constexpr (MASKED) v = ((bits >> (16 * u + e)) & 1u) ? v : kNegInf;
+          x[u * 4 + e] = v;
+        }
+      float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      lmax *= sc;  // sc > 0: the max of scaled scores
+      if (__any(lmax > m_ref[qt] + kRescale)) {  // wave-uniform; first tiles, then rare
+        const float m_new = fmaxf(m_ref[qt], group_max(lmax));
+        const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+        lacc[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+        m_ref[qt] = m_new;
+      }
+      const float neg_m = m_ref[qt] == kNegInf ? 0.0f : -m_ref[qt];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[qt][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[e], sc, neg_m));
+    }
+    // O^T += V^T P^T.  V^T fragments come from transposing LDS reads: lane
+    // (lambda) addresses key kb0 + 4*(lambda/16) + (lambda%16)/4 (+16),
+    // dims dt*16 + 4*(lambda%4).
+    const unsigned char* vh = vl + kb0 * TL::ROWB;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + voff[dt]));
+      const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + 16 * TL::ROWB + voff[dt]));
+      const s16x8 v12 = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, v12);
+#pragma unroll
+      for (int qt = 0; qt < QW; ++qt)
+        o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int qt = 0; qt < QW; ++qt)
+      lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qt], lacc[qt], 0, 0, 0);
+  };
+
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st)
     if (st < n_tiles) issue_tile(st, st);
@@ -324,100 +429,32 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
       const uint16_t *kb_, *vb_;
       tile_rows(t, kb_, vb_, nvalid);
     }
-    // Valid-key bits of this tile for each of the lane's query rows: the first
-    // nvalid keys, and for tree tiles only the ancestors.
-    const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
-    uint64_t vbits[QW];
-#pragma unroll
-    for (int qt = 0; qt < QW; ++qt) {
-      uint64_t v = row_node[qt] >= 0 ? head_bits : 0ull;
-      if (tree_tile) v &= maskw[((wq * QW + qt) * 16 + n16) * 4 + (t - c.n_ptiles)];
-      vbits[qt] = v;
-    }
     const unsigned char* kl = lds + (t % kStages) * TL::STAGEB;
     const unsigned char* vl = kl + TL::TILEB;
-
+    if (!wave_live) {
+      // no real query row in this wave: it only helps with the copies
+    } else if (!tree_tile && nvalid == KT) {
 #pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      if (nwk == 2 && half != wk) continue;
-      const int kb0 = half * 32;
-      if (kb0 >= nvalid) continue;  // wave-uniform: nothing valid in this half
-
-      // S^T = K Q^T: A operand rows = keys kb0 + 16u + n16, dims ks*32 + 8*grp
-      f32x4 s[QW][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int kr = kb0 + 16 * u + n16;
-        bf16x8 kf[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          kf[ks] = *reinterpret_cast<const bf16x8*>(kl + kr * TL::ROWB + 16 * ((ks * 4 + grp) ^ TL::swz_k(kr)));
-#pragma unroll
-        for (int qt = 0; qt < QW; ++qt) {
-          if (!tile_live[qt]) continue;
-          s[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            s[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[qt][ks], s[qt][u], 0, 0, 0);
-        }
+      for (int half = 0; half < 2; ++half) {
+        if (nwk == 2 && half != wk) continue;
+        process_half(std::false_type{}, kl, vl, half * 32, nullptr);
       }
-      bf16x8 pf[QW];
+    } else {
+      // Valid-key bits of this tile per query row: the first nvalid keys, and
+      // for tree tiles only the ancestors.
+      const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+      uint64_t vbits[QW];
 #pragma unroll
       for (int qt = 0; qt < QW; ++qt) {
-        if (!tile_live[qt]) continue;
-        // lane holds scores of query n16 for keys kb0 + 16u + 4*grp + e
-        const uint32_t bits = (uint32_t)(vbits[qt] >> (kb0 + 4 * grp));
-        float x[8];
-        float tmax = kNegInf;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool ok = (bits >> (16 * u + e)) & 1u;
-            const float v = ok ? s[qt][u][e] * a.scale_log2 : kNegInf;
-            x[u * 4 + e] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        tmax = group_max(tmax);
-        const float m_cand = fmaxf(m_ref[qt], tmax);
-        if (__any(m_cand > m_ref[qt] + kRescale)) {  // wave-uniform, rare
-          const float alpha = m_cand == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_cand);
-          l_run[qt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
-          m_ref[qt] = m_cand;
-        }
-        const float m_eff = m_ref[qt] == kNegInf ? 0.0f : m_ref[qt];
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(x[e] - m_eff);
-          psum += p;
-          pf[qt][e] = (__bf16)p;
-        }
-        l_run[qt] += psum;
+        uint64_t v = row_node[qt] >= 0 ? head_bits : 0ull;
+        if (tree_tile) v &= maskw[((wq * QW + qt) * 16 + n16) * 4 + (t - c.n_ptiles)];
+        vbits[qt] = v;
       }
-      // O^T += V^T P^T.  V^T fragments come from transposing LDS reads: lane
-      // (lambda) addresses key kb0 + 4*(lambda/16) + (lambda%16)/4 (+16),
-      // dims dt*16 + 4*(lambda%4).
-      const int vk1 = kb0 + 4 * grp + (n16 >> 2);
-      const int vk2 = vk1 + 16;
-      const int q4 = lane & 3;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int ch = 2 * dt + (q4 >> 1);
-        const int hb = 8 * (q4 & 1);
-        const unsigned char* p1 = vl + vk1 * TL::ROWB + 16 * (ch ^ TL::swz_v(vk1)) + hb;
-        const unsigned char* p2 = vl + vk2 * TL::ROWB + 16 * (ch ^ TL::swz_v(vk2)) + hb;
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-        const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p2);
-        const s16x8 v12 = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, v12);
-#pragma unroll
-        for (int qt = 0; qt < QW; ++qt) {
-          if (!tile_live[qt]) continue;
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
-        }
+#pragma unroll 1
+      for (int half = 0; half < 2; ++half) {
+        if (nwk == 2 && half != wk) continue;
+        if (half * 32 >= nvalid) continue;  // wave-uniform: nothing valid in this half
+        process_half(std::true_type{}, kl, vl, half * 32, vbits);
       }
     }
   }
@@ -437,7 +474,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) slot[k++] = o[qt][dt][e];
         slot[k++] = m_ref[qt];
-        slot[k++] = l_run[qt];
+        slot[k++] = lacc[qt][0];
       }
     }
     __syncthreads();
@@ -457,7 +494,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
       const float a1 = mm == kNegInf ? 1.0f : exp2f(m1 - mm);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = o[qt][dt] * a0 + o1[dt] * a1;
-      l_run[qt] = l_run[qt] * a0 + l1 * a1;
+      lacc[qt][0] = lacc[qt][0] * a0 + l1 * a1;
       m_ref[qt] = mm;
     }
   }
@@ -467,7 +504,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 #pragma unroll
   for (int qt = 0; qt < QW; ++qt) {
     if (!tile_live[qt]) continue;
-    const float lt = group_sum(l_run[qt]);
+    const float lt = lacc[qt][0];
     if (row_node[qt] < 0) continue;
     const int r = r0 + (wq * QW + qt) * 16 + n16;
     if (direct) {
