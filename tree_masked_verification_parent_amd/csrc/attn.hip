@@ -68,7 +68,7 @@ struct AttnDev {
   float* ws_ml;  // [B][Hkv][ns][R][2]
   int64_t cap;
   int B, T, Hq, Hkv, G, R, W;
-  int lmax_bound, kc, ns, nqb, qb_rows, nwg;
+  int lmax_bound, kc, ns, nqb, qb_rows, nunits;
   float scale_log2;
 };
 
@@ -83,18 +83,20 @@ struct WgCtx {
 };
 
 __device__ __forceinline__ bool decode_wg(const AttnDev& a, WgCtx& c) {
-  // XCD-aware remap: hardware id w runs on XCD w % 8; give each XCD a
-  // contiguous range of logical ids (query block fastest).
-  const int per = (a.nwg + 7) / 8;
+  // A unit is one (split, sequence, KV head); units are numbered with the
+  // split slowest, so the full-size first splits are dispatched before the
+  // ragged last ones.  The hardware sends workgroup id w to XCD w % 8: the
+  // nqb query blocks of a unit get ids 8 apart, so they run on one XCD and
+  // share its L2, while consecutive units spread over all XCDs.
   const int w = blockIdx.x;
-  const int logical = (w % 8) * per + (w / 8);
-  if (logical >= a.nwg) return false;
-  c.qb = logical % a.nqb;
-  int rest = logical / a.nqb;
-  c.split = rest % a.ns;
-  rest /= a.ns;
-  c.g = rest % a.Hkv;
-  c.b = rest / a.Hkv;
+  const int span = 8 * a.nqb;
+  const int x = w % 8;
+  const int unit = (w / span) * 8 + x;
+  if (unit >= a.nunits) return false;
+  c.qb = (w % span) / 8;
+  c.g = unit % a.Hkv;
+  c.b = (unit / a.Hkv) % a.B;
+  c.split = unit / (a.Hkv * a.B);
   c.lmax = *a.lmax;
   c.L = a.len[c.b];
   const int st = a.status ? a.status[c.b] : SVT_OK;
@@ -152,7 +154,7 @@ struct Tile {
   __device__ static __forceinline__ int swz_v(int r) { return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1); }
 };
 
-constexpr int kStages = 3;      // LDS ring: one tile computed, two in flight
+constexpr int kStages = 4;      // LDS ring: one tile computed, up to three in flight
 constexpr int kMaxQbRows = 256;  // query rows per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -418,7 +420,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 
   for (int t = 0; t < n_tiles; ++t) {
     // tile t has landed once at most the copies of later tiles are pending
-    if (t + 1 < n_tiles) wait_vmcnt<TL::LOADS>();
+    static_assert(kStages == 4, "wait ladder below assumes 4 stages");
+    const int later = min(kStages - 2, n_tiles - 1 - t);
+    if (later >= 2) wait_vmcnt<2 * TL::LOADS>();
+    else if (later == 1) wait_vmcnt<TL::LOADS>();
     else wait_vmcnt<0>();
     lds_barrier();
     if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1, (t + kStages - 1) % kStages);
@@ -759,11 +764,12 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.qb_rows = p.qb_rows;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   d.scale_log2 = scale * kLog2e;
-  const int64_t nwg = (int64_t)a->B * a->Hkv * p.ns * p.nqb;
-  if (nwg == 0) return hipSuccess;
+  const int64_t nunits = (int64_t)a->B * a->Hkv * p.ns;
+  if (nunits == 0) return hipSuccess;
+  const int64_t nwg = 8 * p.nqb * ((nunits + 7) / 8);
   if (nwg > 0x7FFFFFF0) return hipErrorInvalidValue;
-  d.nwg = (int)nwg;
-  const unsigned grid = (unsigned)(8 * ((nwg + 7) / 8));
+  d.nunits = (int)nunits;
+  const unsigned grid = (unsigned)nwg;
   const dim3 block(256);
   if (a->dtype == SVT_BF16) {
 #define SVT_ATTN_BF16(DD, QQ) hipLaunchKernelGGL((attn_bf16_kernel<DD, QQ>), dim3(grid), block, 0, s, d)
