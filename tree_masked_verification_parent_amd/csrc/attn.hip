@@ -140,21 +140,20 @@ __device__ __forceinline__ void write_seq_status(const AttnDev& a, const WgCtx& 
 // lanes x 16 B, consecutive), so the swizzle is applied on the global side by
 // choosing which chunk each lane fetches.  No tile data passes through
 // registers, and kStages - 1 tiles are in flight while one is computed on.
-template <int D>
+template <int D, int NW>
 struct Tile {
   static constexpr int ROWB = D * 2;
   static constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
   static constexpr int TILEB = KT * ROWB;     // one K or V tile
   static constexpr int STAGEB = 2 * TILEB;
   static constexpr int NINSTR = TILEB / 1024;  // 1 KB copy instructions per K or V tile
-  static constexpr int PER_WAVE = NINSTR / 4;  // per wave
+  static constexpr int PER_WAVE = (NINSTR + NW - 1) / NW;  // per wave (NW waves share a tile)
   static constexpr int LOADS = 2 * PER_WAVE;   // copy instructions per wave per stage
   static constexpr int RPI = 1024 / ROWB;      // rows per copy instruction
   __device__ static __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   __device__ static __forceinline__ int swz_v(int r) { return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1); }
 };
 
-constexpr int kStages = 4;      // LDS ring: one tile computed, up to three in flight
 constexpr int kMaxQbRows = 256;  // query rows per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -197,11 +196,15 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int QW>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
+// NST: depth of the LDS ring (2: one tile in flight, two workgroups fit per CU;
+// 4: three tiles in flight, one workgroup per CU).
+// NW: waves per workgroup (3 or 4).
+template <int D, int QW, int NST, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
+  constexpr int kStages = NST;
   constexpr int NKS = D / 32;  // 32-wide k steps over the head dim
   constexpr int NDT = D / 16;  // 16-wide output dim tiles
-  using TL = Tile<D>;
+  using TL = Tile<D, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * TL::STAGEB];
   __shared__ uint64_t maskw[kMaxQbRows * 4];
 
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 
   // Ancestor-mask words of the block's rows, for the tree tiles.
   if (c.n_ttiles > 0) {
-    for (int x = tid; x < a.qb_rows * a.W; x += 256) {
+    for (int x = tid; x < a.qb_rows * a.W; x += NW * 64) {
       const int rl = x / a.W, w = x % a.W, r = r0 + rl;
       maskw[rl * 4 + w] = r < a.R ? a.mask[((int64_t)c.b * a.T + r % a.T) * a.W + w] : 0ull;
     }
@@ -320,8 +323,21 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
       nvalid = min(KT, a.T - j0);
     }
   };
-  // Copy tile t into stage `st` (every wave issues TL::LOADS instructions).
-  // Rows past the valid ones repeat the last valid row; they are masked out.
+  // Copy tile t into stage `st`.  Every wave issues the same number of copy
+  // instructions (TL::LOADS), so one vmcnt value tracks a tile for all of
+  // them; when NW does not divide the count, a few 1 KB blocks are copied
+  // twice (identical bytes to the same place).  Rows past the valid ones
+  // repeat the last valid row; they are masked out.
+  // Per-lane source rows and swizzled chunk offsets of this wave's copies.
+  int crow[TL::PER_WAVE], ck[TL::PER_WAVE], cv[TL::PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < TL::PER_WAVE; ++j) {
+    const int row = ((wave + NW * j) % TL::NINSTR) * TL::RPI + lane / TL::CPR;
+    const int slot = lane % TL::CPR;
+    crow[j] = row;
+    ck[j] = 8 * (slot ^ TL::swz_k(row));
+    cv[j] = 8 * (slot ^ TL::swz_v(row));
+  }
   auto issue_tile = [&](int t, int st) {
     const uint16_t *kb, *vb;
     int nvalid;
@@ -330,12 +346,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
     unsigned char* vl = kl + TL::TILEB;
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
-      const int ins = wave + 4 * j;
-      const int row = ins * TL::RPI + lane / TL::CPR;
-      const int slot = lane % TL::CPR;
-      const int64_t src = (int64_t)min(row, nvalid - 1) * D;
-      copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
-      copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
+      const int ins = (wave + NW * j) % TL::NINSTR;
+      const int src = (nvalid == KT ? crow[j] : min(crow[j], nvalid - 1)) * D;
+      copy16_to_lds(kb + src + ck[j], kl + ins * 1024);
+      copy16_to_lds(vb + src + cv[j], vl + ins * 1024);
     }
   };
 
@@ -354,6 +368,18 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         kf[u][ks] = *reinterpret_cast<const bf16x8*>(kh + 16 * u * TL::ROWB + koff[ks]);
+    // V^T fragments (transposing LDS reads) are requested now, so that their
+    // latency overlaps the score MFMAs and the softmax.  Lane (lambda)
+    // addresses key kb0 + 4*(lambda/16) + (lambda%16)/4 (+16), dims
+    // dt*16 + 4*(lambda%4).
+    const unsigned char* vh = vl + kb0 * TL::ROWB;
+    bf16x8 vf[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + voff[dt]));
+      const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + 16 * TL::ROWB + voff[dt]));
+      vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
     f32x4 s[QW][2];
 #pragma unroll
     for (int qt = 0; qt < QW; ++qt)
@@ -395,20 +421,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[qt][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[e], sc, neg_m));
     }
-    // O^T += V^T P^T.  V^T fragments come from transposing LDS reads: lane
-    // (lambda) addresses key kb0 + 4*(lambda/16) + (lambda%16)/4 (+16),
-    // dims dt*16 + 4*(lambda%4).
-    const unsigned char* vh = vl + kb0 * TL::ROWB;
+    // O^T += V^T P^T
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + voff[dt]));
-      const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + 16 * TL::ROWB + voff[dt]));
-      const s16x8 v12 = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, v12);
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int qt = 0; qt < QW; ++qt)
-        o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[qt][dt], 0, 0, 0);
-    }
+        o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[qt], o[qt][dt], 0, 0, 0);
 #pragma unroll
     for (int qt = 0; qt < QW; ++qt)
       lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qt], lacc[qt], 0, 0, 0);
@@ -420,10 +438,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnDev a) {
 
   for (int t = 0; t < n_tiles; ++t) {
     // tile t has landed once at most the copies of later tiles are pending
-    static_assert(kStages == 4, "wait ladder below assumes 4 stages");
+    static_assert(kStages == 2 || kStages == 4, "wait ladder covers 2 or 4 stages");
     const int later = min(kStages - 2, n_tiles - 1 - t);
-    if (later >= 2) wait_vmcnt<2 * TL::LOADS>();
-    else if (later == 1) wait_vmcnt<TL::LOADS>();
+    if (kStages == 4 && later >= 2) wait_vmcnt<2 * TL::LOADS>();
+    else if (kStages == 4 && later == 1) wait_vmcnt<TL::LOADS>();
     else wait_vmcnt<0>();
     lds_barrier();
     if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1, (t + kStages - 1) % kStages);
@@ -706,15 +724,23 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   p->R = p->G * p->T;
   p->nqt = (p->R + 15) / 16;
   if (a->dtype == SVT_BF16) {
-    if (p->nqt <= 2) { p->nwk = 2; p->qw = 1; }
-    else if (p->nqt <= 4) { p->nwk = 1; p->qw = 1; }
-    else if (p->nqt <= 8) { p->nwk = 1; p->qw = 2; }
-    else if (p->nqt <= 12) { p->nwk = 1; p->qw = 3; }
-    else { p->nwk = 1; p->qw = 4; }
-    p->qb_rows = (4 / p->nwk) * p->qw * 16;
+    // One or two query tiles: two waves share the rows and split every key
+    // tile.  Otherwise one query tile per wave.  Two-stage rings let two
+    // workgroups share a CU, which hides more latency than a deeper ring.
+    // One query tile per wave, four waves per block; with one or two query
+    // tiles the two waves of a pair split every key tile instead.  (Measured
+    // on the five workloads: deeper rings, more tiles per wave and three-wave
+    // blocks were all slower, because they cost occupancy.)
+    p->nw = 4;
+    p->qw = 1;
+    p->nwk = p->nqt <= 2 ? 2 : 1;
+    p->stages = 2;
+    p->qb_rows = (p->nw / p->nwk) * p->qw * 16;
   } else {
     p->nwk = 1;
     p->qw = 1;
+    p->nw = 4;
+    p->stages = 1;
     p->qb_rows = 64;
   }
   p->nqb = (p->R + p->qb_rows - 1) / p->qb_rows;
@@ -772,22 +798,20 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   const unsigned grid = (unsigned)nwg;
   const dim3 block(256);
   if (a->dtype == SVT_BF16) {
-#define SVT_ATTN_BF16(DD, QQ) hipLaunchKernelGGL((attn_bf16_kernel<DD, QQ>), dim3(grid), block, 0, s, d)
+#define SVT_ATTN_BF16(DD, QQ, SS, WW) \
+  hipLaunchKernelGGL((attn_bf16_kernel<DD, QQ, SS, WW>), dim3(grid), dim3(WW * 64), 0, s, d)
+#define SVT_ATTN_BF16_QW(DD, SS, WW)          \
+  switch (p.qw) {                             \
+    case 1: SVT_ATTN_BF16(DD, 1, SS, WW); break; \
+    case 2: SVT_ATTN_BF16(DD, 2, SS, WW); break; \
+    default: SVT_ATTN_BF16(DD, 3, SS, WW); break; \
+  }
     if (a->D == 128) {
-      switch (p.qw) {
-        case 1: SVT_ATTN_BF16(128, 1); break;
-        case 2: SVT_ATTN_BF16(128, 2); break;
-        case 3: SVT_ATTN_BF16(128, 3); break;
-        default: SVT_ATTN_BF16(128, 4); break;
-      }
+      if (p.stages == 4) { SVT_ATTN_BF16_QW(128, 4, 4) } else { SVT_ATTN_BF16_QW(128, 2, 4) }
     } else {
-      switch (p.qw) {
-        case 1: SVT_ATTN_BF16(64, 1); break;
-        case 2: SVT_ATTN_BF16(64, 2); break;
-        case 3: SVT_ATTN_BF16(64, 3); break;
-        default: SVT_ATTN_BF16(64, 4); break;
-      }
+      if (p.stages == 4) { SVT_ATTN_BF16_QW(64, 4, 4) } else { SVT_ATTN_BF16_QW(64, 2, 4) }
     }
+#undef SVT_ATTN_BF16_QW
 #undef SVT_ATTN_BF16
   } else {
     if (a->D == 128) hipLaunchKernelGGL(attn_fp32_kernel<128>, dim3(grid), block, 0, s, d);
