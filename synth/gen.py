@@ -1,21 +1,56 @@
 """Counter-based random streams and the input generators built on them.
 
+The bulk generators run in a small C core (fastgen.c, same definitions).
 Random bits come from SplitMix64 (Steele, Lea and Flood, "Fast splittable
 pseudorandom number generators", OOPSLA 2014), used counter-style: draw i of
 stream key k is mix(k + (i + 1) * GAMMA).  Normals use the Box-Muller
-transform (one normal from two uniforms).  Everything is vectorised numpy and
+transform (one normal from the two 32-bit halves of one draw).  Everything is vectorised numpy and
 fully determined by (seed, tags).
 """
 from __future__ import annotations
 
+import ctypes
+import os
+import subprocess
+
 import numpy as np
 
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fastgen.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C generator core with gcc (ISO C11, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", _SRC, "-lm", "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _c():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P, u64_, i64_, d_ = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_double
+        L.synth_u64.argtypes = [u64_, i64_, i64_, P]
+        L.synth_normal_f64.argtypes = [u64_, i64_, d_, P]
+        L.synth_normal_f32.argtypes = [u64_, i64_, d_, P]
+        L.synth_normal_bf16.argtypes = [u64_, i64_, d_, P]
+        L.synth_commit_pattern.argtypes = [P, i64_, i64_, i64_, P]
+        _lib = L
+    return _lib
+
 __all__ = [
-    "GAMMA", "mix64", "stream_key", "u64", "uniform01", "normal", "randint",
+    "GAMMA", "mix64", "stream_key", "u64", "uniform01", "normal", "normal_f32", "normal_bf16", "randint",
     "to_bf16_bits", "bf16_bits_to_f32",
     "tree_depth_capped", "tree_bushy", "tree_chain", "tree_star", "tree_relabel",
     "logits_with_designated_top", "plant_drafts", "prefix_lengths",
-    "commit_pattern_bits",
+    "commit_pattern_bits", "commit_pattern_slabs", "commit_pattern_torch",
 ]
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -43,9 +78,10 @@ def stream_key(seed: int, *tags: int) -> np.uint64:
 
 def u64(key, n: int, start: int = 0) -> np.ndarray:
     """Draws start .. start+n-1 of the stream with key `key`."""
-    i = np.arange(start + 1, start + n + 1, dtype=np.uint64)
-    with np.errstate(over="ignore"):
-        return mix64(np.uint64(key) + i * GAMMA)
+    out = np.empty(n, dtype=np.uint64)
+    if n:
+        _c().synth_u64(int(key), start, n, out.ctypes.data_as(ctypes.c_void_p))
+    return out
 
 
 def uniform01(key, n: int, start: int = 0) -> np.ndarray:
@@ -54,11 +90,28 @@ def uniform01(key, n: int, start: int = 0) -> np.ndarray:
 
 
 def normal(key, n: int, sigma: float = 1.0) -> np.ndarray:
-    """n standard normals times sigma (float64), Box-Muller on draws 2i, 2i+1."""
-    r = u64(key, 2 * n)
-    u1 = ((r[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * (1.0 / 9007199254740992.0)
-    u2 = (r[1::2] >> np.uint64(11)).astype(np.float64) * (1.0 / 9007199254740992.0)
-    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2) * sigma
+    """n standard normals times sigma (float64).  Box-Muller on the two 32-bit
+    halves of draw i: u1 = (hi + 1) / 2^32 in (0, 1], u2 = lo / 2^32."""
+    out = np.empty(n, dtype=np.float64)
+    if n:
+        _c().synth_normal_f64(int(key), n, float(sigma), out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def normal_f32(key, n: int, sigma: float = 1.0) -> np.ndarray:
+    """Same values as normal(), rounded to float32."""
+    out = np.empty(n, dtype=np.float32)
+    if n:
+        _c().synth_normal_f32(int(key), n, float(sigma), out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def normal_bf16(key, n: int, sigma: float = 1.0) -> np.ndarray:
+    """Same values as normal_f32(), rounded to bfloat16 (nearest-even); uint16 bits."""
+    out = np.empty(n, dtype=np.uint16)
+    if n:
+        _c().synth_normal_bf16(int(key), n, float(sigma), out.ctypes.data_as(ctypes.c_void_p))
+    return out
 
 
 def randint(key, n: int, lo: int, hi: int, start: int = 0) -> np.ndarray:
@@ -186,3 +239,24 @@ def commit_pattern_bits(slab: np.ndarray, col: np.ndarray, elem: np.ndarray) -> 
     h = (h * 40503) & 0xFFFFFFFF
     h = h ^ (h >> 16)
     return (h & 0xFFFF).astype(np.uint16)
+
+
+def commit_pattern_slabs(slabs, ncol: int, nel: int) -> np.ndarray:
+    """commit_pattern_bits for whole slabs: out[i][c][e] for slab slabs[i]."""
+    sl = np.ascontiguousarray(np.asarray(slabs, dtype=np.int64).reshape(-1))
+    out = np.empty((len(sl), ncol, nel), dtype=np.uint16)
+    if out.size:
+        _c().synth_commit_pattern(sl.ctypes.data_as(ctypes.c_void_p), len(sl), ncol, nel,
+                                  out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def commit_pattern_torch(slab, col, elem):
+    """The same hash on torch int64 tensors (any device), returned as int16
+    bits; used to fill large caches directly in device memory."""
+    h = (slab * 1000003 + col) * 131 + elem
+    h = h ^ (h >> 13)
+    h = (h * 40503) & 0xFFFFFFFF
+    h = h ^ (h >> 16)
+    h = h & 0xFFFF
+    return (h - ((h >> 15) << 16)).to(dtype=__import__("torch").int16)

@@ -115,8 +115,9 @@ def _values(w: Workload, key, shape) -> np.ndarray:
     """Gaussian values of the workload's dtype: float32 array for fp32, uint16
     bfloat16 bits for bf16."""
     n = int(np.prod(shape))
-    x = gen.normal(key, n, w.qkv_sigma).astype(np.float32).reshape(shape)
-    return x if w.dtype == "fp32" else gen.to_bf16_bits(x)
+    if w.dtype == "fp32":
+        return gen.normal_f32(key, n, w.qkv_sigma).reshape(shape)
+    return gen.normal_bf16(key, n, w.qkv_sigma).reshape(shape)
 
 
 def poison_value(w: Workload):
