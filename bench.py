@@ -40,7 +40,43 @@ def parse():
     ap.add_argument("--workload", default="4", help="workload index or name (default: the B=32 ragged round)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB device buffer 3 times (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["attn.hip", "commit.hip", "accept.hip", "mask.hip"]
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tree_masked_verification_parent_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernels):
+    """HBM bytes per launch of the given kernels from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factors), or
+    None when the summary is missing or the kernel sources changed since."""
+    import json as _json
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = _json.load(f)
+    except OSError:
+        return None
+    if t.get("sources_digest") != sources_digest():
+        return None
+    total = 0.0
+    for k in kernels:
+        if k not in t["kernels"]:
+            return None
+        e = t["kernels"][k]
+        total += e["fetch_kib"] * 1024 / t["copy_factor"]["fetch"] + e["write_kib"] * 1024 / t["copy_factor"]["write"]
+    return total
 
 
 def algorithmic_bytes_attention(w, lens, T):
@@ -162,6 +198,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
+        return
     wkey = int(args.workload) if args.workload.isdigit() else args.workload
     w = wl.workload(wkey)
     dtype = torch.float32 if w.dtype == "fp32" else torch.bfloat16
@@ -258,19 +302,22 @@ def main():
         if kind == "commit":
             a = commit_gbps
             return {"kernel": "commit_move_kernel (+ commit_finalize_kernel)", "bound": "hbm", "achieved": a,
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS, "traffic": None,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
+                    "traffic": measured_traffic(["commit_move_kernel"]),
                     "bytes_per_launch": commit_bytes, "avg_launch_us": t_commit * 1e6}
         if kind == "attention":
             a = attn_gbps
             return {"kernel": "attn_bf16_kernel (+ attn_combine_kernel)", "bound": "hbm", "achieved": a,
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS, "traffic": None,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
+                    "traffic": measured_traffic(["attn_bf16_kernel", "attn_combine_kernel"]),
                     "bytes_per_launch": attn_bytes, "avg_launch_us": t_attn * 1e6,
                     "mfma_tflops": attn_flops / t_attn / 1e12,
                     "mfma_frac": attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS}
         if kind == "accept":
             a = acc_bytes / t_accept / 1e9
             return {"kernel": "argmax_partial_kernel (+ accept_kernel)", "bound": "hbm", "achieved": a,
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS, "traffic": None,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
+                    "traffic": measured_traffic(["argmax_partial_kernel", "accept_kernel"]),
                     "bytes_per_launch": acc_bytes, "avg_launch_us": t_accept * 1e6}
         return {"kernel": "build_mask_kernel", "bound": "latency", "achieved": None, "peak": None,
                 "unit": None, "frac": None, "traffic": None, "avg_launch_us": t_mask * 1e6}
