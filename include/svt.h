@@ -181,9 +181,14 @@ int svt_accept(const svt_accept_args* a, hipStream_t stream);
 /*   head, and for tokens_main (with tree_tokens[b][path[b][k]]).             */
 /*   pos_ids[b][c] = c - pad'_b on content, 0 on padding, for c < lmax'.      */
 /*   Columns >= lmax' are not written; padding contents are unspecified.      */
-/* Rows are moved as raw bytes (any bit pattern survives).  If lmax' > cap,   */
-/* or the device-side arguments are inconsistent, nothing is written and      */
-/* commit_status says why.  len and lmax are updated in place.                */
+/* Rows are moved as raw bytes (any bit pattern survives).  Device-side     */
+/* errors are checked over the whole batch in this order, the first one found */
+/* goes to commit_status and then nothing is written:                         */
+/*   SVT_ERR_LENGTH    lmax < 0, lmax > cap, or some len[b] outside [0, lmax] */
+/*   SVT_ERR_ARG       for a sequence with status 0: accept_len[b] or one of  */
+/*                     path[b][0..accept_len[b]] outside [0, M]               */
+/*   SVT_ERR_CAPACITY  lmax' > cap                                            */
+/* Otherwise len and lmax are updated in place.                              */
 /* ------------------------------------------------------------------------ */
 typedef struct svt_commit_args {
   int32_t B, M, Hkv, D, n_layers;
@@ -199,7 +204,7 @@ typedef struct svt_commit_args {
   const int32_t* path;         /* [B][T] from svt_accept                             */
   const int32_t* accept_len;   /* [B] from svt_accept                                */
   const int32_t* status;       /* [B] or NULL                                        */
-  int32_t* commit_status;      /* [1] out: SVT_OK, SVT_ERR_CAPACITY or SVT_ERR_LENGTH */
+  int32_t* commit_status;      /* [1] out: SVT_OK or one of the errors above        */
 } svt_commit_args;
 
 int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream);
