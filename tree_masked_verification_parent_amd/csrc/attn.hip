@@ -175,6 +175,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Makes the compiler complete the loads of x here.  Its wait-count pass does
+// not see the asm copies; a register loaded before the main loop and first
+// read inside it would otherwise get a vmcnt(0) wait inside the loop, which
+// also waits for every prefetched tile.
+template <typename V>
+__device__ __forceinline__ void settle(const V& x) { asm volatile("" ::"v"(x)); }
+
 // Workgroup barrier that does not wait for outstanding global loads (the
 // copies of later tiles stay in flight); pending LDS reads are drained first.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -260,6 +267,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
   // Waves with a real row compute all QW tiles (padding rows have Q = 0 and
   // are never stored), so the MFMA chains need no per-tile branches.
   const bool wave_live = __builtin_amdgcn_readfirstlane(tile_live[0] ? 1 : 0) != 0;
+#pragma unroll
+  for (int t = 0; t < QW; ++t)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) settle(qf[t][ks]);
 
   // Ancestor-mask words of the block's rows, for the tree tiles.
   if (c.n_ttiles > 0) {
@@ -555,6 +566,292 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 }
 
 // --------------------------------------------------------------------------
+// bf16 MFMA kernel, wide form: one workgroup of NW waves holds up to NW*QMAX
+// query tiles of a KV head (all G*T rows when they fit); wave w owns block
+// tiles w, w + NW, ...  Every K/V tile crosses HBM -> LDS once per (sequence,
+// KV head, split) and each K or V fragment read from LDS feeds up to QMAX
+// MFMAs.  A 4-deep ring keeps three tiles in flight (one workgroup per CU);
+// with eight waves two share each SIMD and hide each other's latencies.  Per
+// 64-key tile a wave runs the scores of the whole tile, one softmax step (a
+// single lazy-rescale check per tile), then P V in two 32-key halves.
+// --------------------------------------------------------------------------
+template <int D, int NW, int QMAX>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_wide_kernel(AttnDev a) {
+  constexpr int kStages = 4;
+  constexpr int NKS = D / 32;
+  constexpr int NDT = D / 16;
+  using TL = Tile<D, NW>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * TL::STAGEB];
+  __shared__ uint64_t maskw[kMaxQbRows * 4];
+
+  WgCtx c;
+  if (!decode_wg(a, c)) return;
+  write_seq_status(a, c);
+  if (c.code != SVT_OK) {
+    if (c.split == 0) write_zero_rows<__bf16>(a, c, D);
+    return;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.kcache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.vcache);
+  const uint16_t* __restrict__ ktr = static_cast<const uint16_t*>(a.ktree);
+  const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
+  const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
+  const int r0 = c.qb * a.qb_rows;   // qb_rows = 16 * tiles per workgroup
+  const int tpb = a.qb_rows / 16;
+
+  // This wave's tiles are block tiles wave + NW*t, t < QMAX; the live ones
+  // come first.
+  bf16x8 qf[QMAX][NKS];
+  int row_node[QMAX], row_head[QMAX];
+  bool tile_live[QMAX];
+  int nlive = 0;  // wave-uniform
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t) {
+    const int lt = wave + NW * t;
+    tile_live[t] = lt < tpb && r0 + lt * 16 < a.R;
+    nlive += tile_live[t] ? 1 : 0;
+    const int r = r0 + lt * 16 + n16;
+    const bool ok = tile_live[t] && r < a.R;
+    row_node[t] = ok ? r % a.T : -1;
+    row_head[t] = ok ? c.g * a.G + r / a.T : 0;
+    const uint16_t* qrow = q + (((int64_t)c.b * a.T + (ok ? row_node[t] : 0)) * a.Hq + row_head[t]) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ok) {
+        qf[t][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[t][ks][e] = (__bf16)0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) settle(qf[t][ks]);
+
+  if (c.n_ttiles > 0) {
+    for (int x = tid; x < a.qb_rows * a.W; x += NW * 64) {
+      const int rl = x / a.W, w = x % a.W, r = r0 + rl;
+      maskw[rl * 4 + w] = r < a.R ? a.mask[((int64_t)c.b * a.T + r % a.T) * a.W + w] : 0ull;
+    }
+  }
+  __syncthreads();
+
+  // Softmax state as in the narrow kernel: base-2 units, lazy reference,
+  // row sums from an all-ones MFMA.
+  f32x4 o[QMAX][NDT];
+  f32x4 lacc[QMAX];
+  float m_ref[QMAX];
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t) {
+    m_ref[t] = row_node[t] >= 0 ? kNegInf : 0.0f;
+    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const float sc = a.scale_log2;
+
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = n16 * TL::ROWB + 16 * ((ks * 4 + grp) ^ TL::swz_k(n16));
+  const int vrow = 4 * grp + (n16 >> 2);
+  const int q4 = lane & 3;
+  int voff[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+    voff[dt] = vrow * TL::ROWB + 16 * ((2 * dt + (q4 >> 1)) ^ TL::swz_v(vrow)) + 8 * (q4 & 1);
+
+  const int n_tiles = c.n_ptiles + c.n_ttiles;
+  const int pad = c.lmax - c.L;
+
+  auto tile_rows = [&](int t, const uint16_t*& kb, const uint16_t*& vb, int& nvalid) {
+    if (t < c.n_ptiles) {
+      const int k0 = c.k_beg + t * KT;
+      const int64_t col = (int64_t)pad + k0;
+      kb = kc + (bg * a.cap + col) * D;
+      vb = vc + (bg * a.cap + col) * D;
+      nvalid = min(KT, c.k_end - k0);
+    } else {
+      const int j0 = (t - c.n_ptiles) * KT;
+      kb = ktr + (bg * a.T + j0) * D;
+      vb = vtr + (bg * a.T + j0) * D;
+      nvalid = min(KT, a.T - j0);
+    }
+  };
+  // Copy source offsets are recomputed per tile (a few integer ops) rather
+  // than kept live through the loop.
+  auto issue_tile = [&](int t, int st) {
+    const uint16_t *kb, *vb;
+    int nvalid;
+    tile_rows(t, kb, vb, nvalid);
+    unsigned char* kl = lds + st * TL::STAGEB;
+    unsigned char* vl = kl + TL::TILEB;
+#pragma unroll
+    for (int j = 0; j < TL::PER_WAVE; ++j) {
+      const int ins = (wave + NW * j) % TL::NINSTR;
+      const int row = ins * TL::RPI + lane / TL::CPR;
+      const int slot = lane % TL::CPR;
+      const int src = (nvalid == KT ? row : min(row, nvalid - 1)) * D;
+      copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
+      copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
+    }
+  };
+
+  // The tile loop for a wave with NQ live query tiles.  Each wave runs one
+  // instance, so the accumulators keep their registers through the loop
+  // (several bodies inside one loop would make the compiler copy them at
+  // every merge).  Per tile: s[qt][u] = scores of keys 16u + 4*grp + e for
+  // query n16; ragged or tree tiles set the invalid ones to -inf in place;
+  // P of keys 32h + ... is pf[qt][h].
+  auto run = [&](auto nq_c) {
+    constexpr int NQ = decltype(nq_c)::value;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int later = min(kStages - 2, n_tiles - 1 - t);
+      if (later >= 2) wait_vmcnt<2 * TL::LOADS>();
+      else if (later == 1) wait_vmcnt<TL::LOADS>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1, (t + kStages - 1) % kStages);
+      if constexpr (NQ > 0) {
+        const bool tree_tile = t >= c.n_ptiles;
+        const int nvalid = tree_tile ? min(KT, a.T - (t - c.n_ptiles) * KT) : min(KT, c.k_end - (c.k_beg + t * KT));
+        const unsigned char* kl = lds + (t % kStages) * TL::STAGEB;
+        const unsigned char* vl = kl + TL::TILEB;
+
+        f32x4 sacc[NQ][4];
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sacc[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 kf[2][NKS];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+              kf[u][ks] = *reinterpret_cast<const bf16x8*>(kl + (32 * h + 16 * u) * TL::ROWB + koff[ks]);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int qt = 0; qt < NQ; ++qt)
+                sacc[qt][2 * h + u] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], sacc[qt][2 * h + u], 0, 0, 0);
+        }
+        if (tree_tile || nvalid < KT) {  // wave-uniform, rare
+          const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt) {
+            uint64_t v = row_node[qt] >= 0 ? head_bits : 0ull;
+            if (tree_tile) v &= maskw[((wave + NW * qt) * 16 + n16) * 4 + (t - c.n_ptiles)];
+            const uint64_t bits = v >> (4 * grp);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (!((bits >> (16 * u + e)) & 1ull)) sacc[qt][u][e] = kNegInf;
+          }
+        }
+        bf16x8 pf[NQ][2];
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) {
+          float mx = sacc[qt][0][0];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[qt][u][e]);
+          mx *= sc;
+          if (__any(mx > m_ref[qt] + kRescale)) {
+            const float m_new = fmaxf(m_ref[qt], group_max(mx));
+            const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+            lacc[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+            m_ref[qt] = m_new;
+          }
+          const float neg_m = m_ref[qt] == kNegInf ? 0.0f : -m_ref[qt];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              pf[qt][h][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qt][2 * h + e / 4][e % 4], sc, neg_m));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const unsigned char* vh = vl + 32 * h * TL::ROWB;
+          bf16x8 vf[NDT];
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + voff[dt]));
+            const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + 16 * TL::ROWB + voff[dt]));
+            vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int qt = 0; qt < NQ; ++qt)
+              o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[qt][h], o[qt][dt], 0, 0, 0);
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt)
+            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qt][h], lacc[qt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < n_tiles) issue_tile(st, st);
+  if (QMAX >= 2 && nlive == 2) run(std::integral_constant<int, (QMAX >= 2 ? 2 : 1)>{});
+  else if (nlive == 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
+
+  // ---- epilogue: lane holds O^T[d = dt*16 + 4*grp + e][query n16]
+  const bool direct = c.ns_b == 1;
+#pragma unroll
+  for (int qt = 0; qt < QMAX; ++qt) {
+    if (!tile_live[qt] || row_node[qt] < 0) continue;
+    const float lt = lacc[qt][0];
+    const int r = r0 + (wave + NW * qt) * 16 + n16;
+    if (direct) {
+      const float inv = 1.0f / lt;
+      __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)c.b * a.T + row_node[qt]) * a.Hq + row_head[qt]) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[qt][dt][e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * grp) = v;
+      }
+    } else {
+      const int64_t pr = ((bg * a.ns + c.split) * a.R + r);
+      float* po = a.ws_o + pr * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[qt][dt];
+      if (grp == 0) {
+        a.ws_ml[pr * 2 + 0] = m_ref[qt];
+        a.ws_ml[pr * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // fp32 VALU kernel: 64 query rows per workgroup, 16 per wave.
 // --------------------------------------------------------------------------
 template <int D>
@@ -731,12 +1028,28 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     // tiles the two waves of a pair split every key tile instead.  (Measured
     // on the five workloads: deeper rings, more tiles per wave and three-wave
     // blocks were all slower, because they cost occupancy.)
-    p->nw = 4;
-    p->qw = 1;
-    p->nwk = p->nqt <= 2 ? 2 : 1;
-    p->stages = 2;
-    p->qb_rows = (p->nw / p->nwk) * p->qw * 16;
+    if (p->nqt <= 2) {
+      p->wide = 0;
+      p->nw = 4;
+      p->qw = 1;
+      p->nwk = 2;
+      p->stages = 2;
+      p->qb_rows = (p->nw / p->nwk) * p->qw * 16;
+    } else {
+      // Wide form: up to 16 query tiles per workgroup, spread evenly over the
+      // fewest workgroups per KV head; four waves for up to four tiles, else
+      // eight (two per SIMD) with one or two tiles each.
+      const int nqb = (p->nqt + 15) / 16;
+      const int tpb = (p->nqt + nqb - 1) / nqb;
+      p->wide = 1;
+      p->nw = tpb <= 4 ? 4 : 8;
+      p->qw = (tpb + p->nw - 1) / p->nw;
+      p->nwk = 1;
+      p->stages = 4;
+      p->qb_rows = tpb * 16;
+    }
   } else {
+    p->wide = 0;
     p->nwk = 1;
     p->qw = 1;
     p->nw = 4;
@@ -748,9 +1061,10 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   // fewer when the workgroups are heavy (their partials cost more).
   const int64_t ptiles = ((int64_t)a->lmax_bound + KT - 1) / KT;
   const int64_t units = ptiles * a->B * a->Hkv * p->nqb;
-  const int64_t target = (p->qw >= 4) ? 512 : 1024;
-  int64_t tiles_per_split = (units + target - 1) / (target > 0 ? target : 1);
-  if (tiles_per_split < 4) tiles_per_split = 4;
+  const int64_t target = p->wide ? 1536 : 1024;
+  const int64_t min_tiles = p->wide ? 8 : 4;
+  int64_t tiles_per_split = (units + target - 1) / target;
+  if (tiles_per_split < min_tiles) tiles_per_split = min_tiles;
   p->kc = (int)(tiles_per_split * KT);
   p->ns = a->lmax_bound > 0 ? (int)((a->lmax_bound + p->kc - 1) / p->kc) : 1;
   if (p->ns < 1) p->ns = 1;
@@ -800,17 +1114,19 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   if (a->dtype == SVT_BF16) {
 #define SVT_ATTN_BF16(DD, QQ, SS, WW) \
   hipLaunchKernelGGL((attn_bf16_kernel<DD, QQ, SS, WW>), dim3(grid), dim3(WW * 64), 0, s, d)
-#define SVT_ATTN_BF16_QW(DD, SS, WW)          \
-  switch (p.qw) {                             \
-    case 1: SVT_ATTN_BF16(DD, 1, SS, WW); break; \
-    case 2: SVT_ATTN_BF16(DD, 2, SS, WW); break; \
-    default: SVT_ATTN_BF16(DD, 3, SS, WW); break; \
-  }
-    if (a->D == 128) {
-      if (p.stages == 4) { SVT_ATTN_BF16_QW(128, 4, 4) } else { SVT_ATTN_BF16_QW(128, 2, 4) }
+#define SVT_ATTN_BF16_QW(DD, SS, WW) SVT_ATTN_BF16(DD, 1, SS, WW);
+#define SVT_ATTN_WIDE(DD)                                                                             \
+  if (p.nw == 4) hipLaunchKernelGGL((attn_bf16_wide_kernel<DD, 4, 1>), dim3(grid), dim3(256), 0, s, d);   \
+  else if (p.qw == 1) hipLaunchKernelGGL((attn_bf16_wide_kernel<DD, 8, 1>), dim3(grid), dim3(512), 0, s, d); \
+  else hipLaunchKernelGGL((attn_bf16_wide_kernel<DD, 8, 2>), dim3(grid), dim3(512), 0, s, d);
+    if (p.wide) {
+      if (a->D == 128) { SVT_ATTN_WIDE(128) } else { SVT_ATTN_WIDE(64) }
+    } else if (a->D == 128) {
+      SVT_ATTN_BF16_QW(128, 2, 4)
     } else {
-      if (p.stages == 4) { SVT_ATTN_BF16_QW(64, 4, 4) } else { SVT_ATTN_BF16_QW(64, 2, 4) }
+      SVT_ATTN_BF16_QW(64, 2, 4)
     }
+#undef SVT_ATTN_WIDE
 #undef SVT_ATTN_BF16_QW
 #undef SVT_ATTN_BF16
   } else {
