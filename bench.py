@@ -307,9 +307,9 @@ def main():
                     "bytes_per_launch": commit_bytes, "avg_launch_us": t_commit * 1e6}
         if kind == "attention":
             a = attn_gbps
-            return {"kernel": "attn_bf16_kernel (+ attn_combine_kernel)", "bound": "hbm", "achieved": a,
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
-                    "traffic": measured_traffic(["attn_bf16_kernel", "attn_combine_kernel"]),
+            return {"kernel": "attn_bf16_stream_kernel (+ attn_stream_combine_kernel)", "bound": "hbm",
+                    "achieved": a, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
+                    "traffic": measured_traffic(["attn_bf16_stream_kernel", "attn_stream_combine_kernel"]),
                     "bytes_per_launch": attn_bytes, "avg_launch_us": t_attn * 1e6,
                     "mfma_tflops": attn_flops / t_attn / 1e12,
                     "mfma_frac": attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS}

@@ -124,7 +124,19 @@ typedef struct svt_attn_args {
                              /* fails.  Such sequences get all-zero output.           */
   void* workspace;           /* device scratch, svt_verify_attention_workspace bytes  */
   size_t workspace_bytes;
+  int32_t form;              /* svt_attn_form: which work decomposition (bf16 only)   */
 } svt_attn_args;
+
+/* Work decomposition of svt_verify_attention (bf16; fp32 always splits).
+ * Both compute the same function; results agree to rounding, and each is
+ * bitwise reproducible for identical inputs.
+ *   SVT_ATTN_AUTO    choose by shape
+ *   SVT_ATTN_SPLIT   fixed key splits per (sequence, KV head); a sequence's
+ *                    result does not depend on the rest of the batch
+ *   SVT_ATTN_STREAM  the key tiles of the whole batch cut into one equal
+ *                    range per compute unit (needs three or more 16-row query
+ *                    tiles per KV head and B <= 2048, else SVT_ERR_UNSUPPORTED) */
+typedef enum svt_attn_form { SVT_ATTN_AUTO = 0, SVT_ATTN_SPLIT = 1, SVT_ATTN_STREAM = 2 } svt_attn_form;
 
 /* Bytes of workspace svt_verify_attention needs for these shapes (pointer
  * fields are ignored).  0 for invalid arguments. */

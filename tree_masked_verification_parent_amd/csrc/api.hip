@@ -53,12 +53,16 @@ size_t svt_verify_attention_workspace(const svt_attn_args* a) {
 int svt_verify_attention(const svt_attn_args* a, hipStream_t stream) {
   char shape[160];
   if (!a) return finish("svt_verify_attention", SVT_ERR_ARG, "null args");
-  std::snprintf(shape, sizeof shape, "B=%d M=%d Hq=%d Hkv=%d D=%d dtype=%d cap=%lld lmax_bound=%d", a->B, a->M,
-                a->Hq, a->Hkv, a->D, a->dtype, (long long)a->cap, a->lmax_bound);
+  std::snprintf(shape, sizeof shape, "B=%d M=%d Hq=%d Hkv=%d D=%d dtype=%d cap=%lld lmax_bound=%d form=%d", a->B,
+                a->M, a->Hq, a->Hkv, a->D, a->dtype, (long long)a->cap, a->lmax_bound, a->form);
   if (a->B < 0 || a->M < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0 || a->cap < 0 ||
       a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap || !(a->scale >= 0.0f))
     return finish("svt_verify_attention", SVT_ERR_ARG, shape);
+  if (a->form < SVT_ATTN_AUTO || a->form > SVT_ATTN_STREAM) return finish("svt_verify_attention", SVT_ERR_ARG, shape);
   if (a->M >= SVT_MAX_T || (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
+    return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);
+  if (a->form == SVT_ATTN_STREAM &&
+      (a->dtype != SVT_BF16 || ((a->Hq / a->Hkv) * (a->M + 1) + 15) / 16 < 3 || a->B > 2048))
     return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);
   if (a->B == 0) return finish("svt_verify_attention", SVT_OK, shape);
   if (!a->q || !a->k_cache || !a->v_cache || !a->len || !a->lmax || !a->k_tree || !a->v_tree || !a->mask ||

@@ -64,11 +64,13 @@ struct AttnDev {
   const int32_t* status;
   void* out;
   int32_t* seq_status;
-  float* ws_o;   // [B][Hkv][ns][R][D]
-  float* ws_ml;  // [B][Hkv][ns][R][2]
+  float* ws_o;   // split partials [B][Hkv][ns][R][D]; stream partials [2*grid][qb_rows][D]
+  float* ws_ml;  // matching (m, l) pairs
+  int* ws_pref;  // stream form: tiles before each sequence, [B + 1]
   int64_t cap;
   int B, T, Hq, Hkv, G, R, W;
   int lmax_bound, kc, ns, nqb, qb_rows, nunits;
+  int stream_grid;  // workgroups of the stream form
   float scale_log2;
 };
 
@@ -566,102 +568,173 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 }
 
 // --------------------------------------------------------------------------
-// bf16 MFMA kernel, wide form: one workgroup of NW waves holds up to NW*QMAX
-// query tiles of a KV head (all G*T rows when they fit); wave w owns block
-// tiles w, w + NW, ...  Every K/V tile crosses HBM -> LDS once per (sequence,
-// KV head, split) and each K or V fragment read from LDS feeds up to QMAX
-// MFMAs.  A 4-deep ring keeps three tiles in flight (one workgroup per CU);
-// with eight waves two share each SIMD and hide each other's latencies.  Per
-// 64-key tile a wave runs the scores of the whole tile, one softmax step (a
-// single lazy-rescale check per tile), then P V in two 32-key halves.
+// bf16 MFMA kernel, stream form (used when a KV head has three or more query
+// tiles).  A work unit is one (sequence, KV head, query block): up to 12
+// query tiles of 16 rows, one per wave, so every K/V tile of the unit crosses
+// HBM -> LDS once and feeds all of its query rows.  A unit's key tiles are its
+// prefix tiles followed by its tree tiles; the tiles of all units, concatenated
+// in unit order, form one stream that is cut into gridDim.x equal ranges, one
+// per workgroup (one workgroup per CU).  A workgroup walks its range with one
+// 4-deep DMA ring that runs across unit boundaries.  A unit lying wholly inside
+// one range is normalised and written directly; a unit cut by range ends
+// leaves (m, l, O) partials in two slots per workgroup (slot 2c: a piece that
+// ends at its unit's end, slot 2c+1: the piece that ends at the range end), and
+// attn_stream_combine_kernel merges them in stream order.  No workgroup waits
+// for another, and the result does not depend on timing.
 // --------------------------------------------------------------------------
-template <int D, int NW, int QMAX>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_wide_kernel(AttnDev a) {
+constexpr int kStreamMaxB = 2048;
+
+// Key tiles one unit of sequence b holds (prefix tiles + tree tiles), or 0
+// when the sequence is skipped; *code says why.
+__device__ __forceinline__ int stream_seq_tiles(const AttnDev& a, int b, int lmax, int* code) {
+  const int st = a.status ? a.status[b] : SVT_OK;
+  const int L = a.len[b];
+  const bool len_ok = lmax >= 0 && lmax <= a.lmax_bound && L >= 0 && L <= lmax;
+  *code = st != SVT_OK ? st : (len_ok ? SVT_OK : SVT_ERR_LENGTH);
+  return *code == SVT_OK ? (L + KT - 1) / KT + (a.T + KT - 1) / KT : 0;
+}
+
+// Stream position of the first tile of workgroup range c (ranges are floor(c*N/G)).
+__device__ __forceinline__ int64_t stream_lo(int64_t c, int64_t n, int g) { return c * n / g; }
+// Range holding stream tile x.
+__device__ __forceinline__ int stream_range_of(int64_t x, int64_t n, int g) { return (int)(((x + 1) * g - 1) / n); }
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
   constexpr int kStages = 4;
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
+  constexpr int NT = NW * 64;
   using TL = Tile<D, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * TL::STAGEB];
-  __shared__ uint64_t maskw[kMaxQbRows * 4];
-
-  WgCtx c;
-  if (!decode_wg(a, c)) return;
-  write_seq_status(a, c);
-  if (c.code != SVT_OK) {
-    if (c.split == 0) write_zero_rows<__bf16>(a, c, D);
-    return;
-  }
+  __shared__ int s_pref[kStreamMaxB + 1];  // s_pref[b] = tiles of sequences < b (per unit)
+  __shared__ int s_len[kStreamMaxB];
+  __shared__ int s_wsum[NW];
+  __shared__ int s_carry;
+  __shared__ uint64_t s_mask[NW * 2 * 16][4];  // each lane's tree-mask words, its own rows only
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n16 = lane & 15;
   const int grp = lane >> 4;
+  const int B = a.B;
+  const int lmax = *a.lmax;
+
+  // ---- per-sequence tile counts and their prefix (every workgroup computes it)
+  if (tid == 0) {
+    s_pref[0] = 0;
+    s_carry = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < B; base += NT) {
+    const int b = base + tid;
+    int v = 0, code;
+    if (b < B) {
+      v = stream_seq_tiles(a, b, lmax, &code);
+      s_len[b] = a.len[b];
+    }
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    int off = s_carry;
+    for (int w = 0; w < wave; ++w) off += s_wsum[w];
+    if (b < B) s_pref[b + 1] = off + x;
+    __syncthreads();
+    if (tid == NT - 1) s_carry = off + x;
+    __syncthreads();
+  }
+  const int G = gridDim.x;
+  // Consecutive ranges go to one XCD (the hardware sends workgroup w to XCD
+  // w % 8), so the query blocks of one KV head, adjacent in the stream, tend
+  // to share an L2.
+  const int c = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int UPB = a.Hkv * a.nqb;  // units per sequence
+  const int64_t N = (int64_t)UPB * s_pref[B];
+  const int64_t lo = stream_lo(c, N, G), hi = stream_lo(c + 1, N, G);
+  if (c == 0 && a.ws_pref)
+    for (int b = tid; b <= B; b += NT) a.ws_pref[b] = s_pref[b];
+
+  // Cursor over the stream: unit (b, j = g*nqb + qb), its first tile `base`
+  // and its tile count.  All fields are wave-uniform.
+  struct Cur {
+    int b, j, ntl;
+    int64_t base;
+  };
+  auto locate = [&](int64_t x) {
+    int l = 0, h = B;
+    while (h - l > 1) {
+      const int m = (l + h) >> 1;
+      if ((int64_t)UPB * s_pref[m] <= x) l = m;
+      else h = m;
+    }
+    Cur r;
+    r.b = __builtin_amdgcn_readfirstlane(l);
+    r.ntl = __builtin_amdgcn_readfirstlane(s_pref[r.b + 1] - s_pref[r.b]);
+    const int64_t sb = (int64_t)UPB * s_pref[r.b];
+    r.j = (int)((x - sb) / r.ntl);
+    r.base = sb + (int64_t)r.j * r.ntl;
+    return r;
+  };
+  auto advance = [&](Cur& r) {
+    r.base += r.ntl;
+    if (++r.j == UPB) {
+      r.j = 0;
+      do {
+        ++r.b;
+      } while (r.b < B && s_pref[r.b + 1] == s_pref[r.b]);
+      r.ntl = r.b < B ? __builtin_amdgcn_readfirstlane(s_pref[r.b + 1] - s_pref[r.b]) : 0;
+    }
+  };
 
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.kcache);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.vcache);
   const uint16_t* __restrict__ ktr = static_cast<const uint16_t*>(a.ktree);
   const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
-  const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
-  const int r0 = c.qb * a.qb_rows;   // qb_rows = 16 * tiles per workgroup
   const int tpb = a.qb_rows / 16;
 
-  // This wave's tiles are block tiles wave + NW*t, t < QMAX; the live ones
-  // come first.
-  bf16x8 qf[QMAX][NKS];
-  int row_node[QMAX], row_head[QMAX];
-  bool tile_live[QMAX];
-  int nlive = 0;  // wave-uniform
-#pragma unroll
-  for (int t = 0; t < QMAX; ++t) {
-    const int lt = wave + NW * t;
-    tile_live[t] = lt < tpb && r0 + lt * 16 < a.R;
-    nlive += tile_live[t] ? 1 : 0;
-    const int r = r0 + lt * 16 + n16;
-    const bool ok = tile_live[t] && r < a.R;
-    row_node[t] = ok ? r % a.T : -1;
-    row_head[t] = ok ? c.g * a.G + r / a.T : 0;
-    const uint16_t* qrow = q + (((int64_t)c.b * a.T + (ok ? row_node[t] : 0)) * a.Hq + row_head[t]) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (ok) {
-        qf[t][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + grp * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[t][ks][e] = (__bf16)0.0f;
-      }
+  // Source rows of stream tile x of unit `r`; tree_t = -1 for a prefix tile.
+  auto tile_src = [&](const Cur& r, int64_t x, const uint16_t*& kb, const uint16_t*& vb, int& nvalid, int& tree_t) {
+    const int t = (int)(x - r.base);
+    const int L = s_len[r.b];
+    const int np = (L + KT - 1) / KT;
+    const int64_t bg = (int64_t)r.b * a.Hkv + r.j / a.nqb;
+    if (t < np) {
+      const int64_t col = (int64_t)(lmax - L) + (int64_t)t * KT;
+      kb = kc + (bg * a.cap + col) * D;
+      vb = vc + (bg * a.cap + col) * D;
+      nvalid = min(KT, L - t * KT);
+      tree_t = -1;
+    } else {
+      const int j0 = (t - np) * KT;
+      kb = ktr + (bg * a.T + j0) * D;
+      vb = vtr + (bg * a.T + j0) * D;
+      nvalid = min(KT, a.T - j0);
+      tree_t = t - np;
     }
-  }
+  };
+  auto issue_tile = [&](const Cur& r, int64_t x, int st) {
+    const uint16_t *kb, *vb;
+    int nvalid, tree_t;
+    tile_src(r, x, kb, vb, nvalid, tree_t);
+    unsigned char* kl = lds + st * TL::STAGEB;
+    unsigned char* vl = kl + TL::TILEB;
 #pragma unroll
-  for (int t = 0; t < QMAX; ++t)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) settle(qf[t][ks]);
-
-  if (c.n_ttiles > 0) {
-    for (int x = tid; x < a.qb_rows * a.W; x += NW * 64) {
-      const int rl = x / a.W, w = x % a.W, r = r0 + rl;
-      maskw[rl * 4 + w] = r < a.R ? a.mask[((int64_t)c.b * a.T + r % a.T) * a.W + w] : 0ull;
+    for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
+      const int ins = (wave + NW * jj) % TL::NINSTR;
+      const int row = ins * TL::RPI + lane / TL::CPR;
+      const int slot = lane % TL::CPR;
+      const int src = (nvalid == KT ? row : min(row, nvalid - 1)) * D;
+      copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
+      copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
     }
-  }
-  __syncthreads();
-
-  // Softmax state as in the narrow kernel: base-2 units, lazy reference,
-  // row sums from an all-ones MFMA.
-  f32x4 o[QMAX][NDT];
-  f32x4 lacc[QMAX];
-  float m_ref[QMAX];
-#pragma unroll
-  for (int t = 0; t < QMAX; ++t) {
-    m_ref[t] = row_node[t] >= 0 ? kNegInf : 0.0f;
-    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-  const float sc = a.scale_log2;
+  };
 
   int koff[NKS];
 #pragma unroll
@@ -672,92 +745,78 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_wide_kernel(AttnDev a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
     voff[dt] = vrow * TL::ROWB + 16 * ((2 * dt + (q4 >> 1)) ^ TL::swz_v(vrow)) + 8 * (q4 & 1);
-
-  const int n_tiles = c.n_ptiles + c.n_ttiles;
-  const int pad = c.lmax - c.L;
-
-  auto tile_rows = [&](int t, const uint16_t*& kb, const uint16_t*& vb, int& nvalid) {
-    if (t < c.n_ptiles) {
-      const int k0 = c.k_beg + t * KT;
-      const int64_t col = (int64_t)pad + k0;
-      kb = kc + (bg * a.cap + col) * D;
-      vb = vc + (bg * a.cap + col) * D;
-      nvalid = min(KT, c.k_end - k0);
-    } else {
-      const int j0 = (t - c.n_ptiles) * KT;
-      kb = ktr + (bg * a.T + j0) * D;
-      vb = vtr + (bg * a.T + j0) * D;
-      nvalid = min(KT, a.T - j0);
-    }
-  };
-  // Copy source offsets are recomputed per tile (a few integer ops) rather
-  // than kept live through the loop.
-  auto issue_tile = [&](int t, int st) {
-    const uint16_t *kb, *vb;
-    int nvalid;
-    tile_rows(t, kb, vb, nvalid);
-    unsigned char* kl = lds + st * TL::STAGEB;
-    unsigned char* vl = kl + TL::TILEB;
+  bf16x8 ones;
 #pragma unroll
-    for (int j = 0; j < TL::PER_WAVE; ++j) {
-      const int ins = (wave + NW * j) % TL::NINSTR;
-      const int row = ins * TL::RPI + lane / TL::CPR;
-      const int slot = lane % TL::CPR;
-      const int src = (nvalid == KT ? row : min(row, nvalid - 1)) * D;
-      copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
-      copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
-    }
-  };
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const float sc = a.scale_log2;
 
-  // The tile loop for a wave with NQ live query tiles.  Each wave runs one
-  // instance, so the accumulators keep their registers through the loop
-  // (several bodies inside one loop would make the compiler copy them at
-  // every merge).  Per tile: s[qt][u] = scores of keys 16u + 4*grp + e for
-  // query n16; ragged or tree tiles set the invalid ones to -inf in place;
-  // P of keys 32h + ... is pf[qt][h].
-  auto run = [&](auto nq_c) {
+  // Per-piece state of this wave's query tiles (block tiles wave, wave + NW).
+  bf16x8 qf[2][NKS];
+  f32x4 o[2][NDT];
+  f32x4 lacc[2];
+  float m_ref[2];
+  int row_node[2], row_head[2];
+
+  Cur cur{0, 0, 0, 0}, pcur{0, 0, 0, 0};
+  if (lo < hi) {
+    cur = locate(lo);
+    pcur = cur;
+  }
+  // Producer: a cursor kStages - 1 tiles ahead of the consumer.
+  int64_t px = lo;
+  auto produce = [&](int st) {
+    if (px == pcur.base + pcur.ntl) advance(pcur);
+    issue_tile(pcur, px, st);
+    ++px;
+  };
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (lo + st < hi) produce(st);
+
+  // The tile loop of one piece, for a wave with NQ live query tiles.  Each
+  // piece runs one instance, so the accumulators keep their registers.
+  auto run_piece = [&](auto nq_c, int64_t x0, int64_t x1) {
     constexpr int NQ = decltype(nq_c)::value;
-    for (int t = 0; t < n_tiles; ++t) {
-      const int later = min(kStages - 2, n_tiles - 1 - t);
-      if (later >= 2) wait_vmcnt<2 * TL::LOADS>();
-      else if (later == 1) wait_vmcnt<TL::LOADS>();
+    for (int64_t x = x0; x < x1; ++x) {
+      const int64_t rem = hi - 1 - x;
+      if (rem >= 2) wait_vmcnt<2 * TL::LOADS>();
+      else if (rem == 1) wait_vmcnt<TL::LOADS>();
       else wait_vmcnt<0>();
       lds_barrier();
-      if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1, (t + kStages - 1) % kStages);
+      if (x + kStages - 1 < hi) produce((int)((x - lo + kStages - 1) % kStages));
       if constexpr (NQ > 0) {
-        const bool tree_tile = t >= c.n_ptiles;
-        const int nvalid = tree_tile ? min(KT, a.T - (t - c.n_ptiles) * KT) : min(KT, c.k_end - (c.k_beg + t * KT));
-        const unsigned char* kl = lds + (t % kStages) * TL::STAGEB;
+        const uint16_t *kb_, *vb_;
+        int nvalid, tree_t;
+        tile_src(cur, x, kb_, vb_, nvalid, tree_t);
+        const unsigned char* kl = lds + ((x - lo) % kStages) * TL::STAGEB;
         const unsigned char* vl = kl + TL::TILEB;
-
+        // All K fragments of the tile are requested before the first score MFMA.
+        bf16x8 kf[4][NKS];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            kf[u][ks] = *reinterpret_cast<const bf16x8*>(kl + 16 * u * TL::ROWB + koff[ks]);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 sacc[NQ][4];
 #pragma unroll
         for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
           for (int u = 0; u < 4; ++u) sacc[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 kf[2][NKS];
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-              kf[u][ks] = *reinterpret_cast<const bf16x8*>(kl + (32 * h + 16 * u) * TL::ROWB + koff[ks]);
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-              for (int qt = 0; qt < NQ; ++qt)
-                sacc[qt][2 * h + u] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], sacc[qt][2 * h + u], 0, 0, 0);
-        }
-        if (tree_tile || nvalid < KT) {  // wave-uniform, rare
+            for (int qt = 0; qt < NQ; ++qt)
+              sacc[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], sacc[qt][u], 0, 0, 0);
+        // sacc[qt][u][e] = score of key 16u + 4*grp + e of the tile for query n16.
+        if (tree_t >= 0 || nvalid < KT) {  // wave-uniform, rare
           const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
 #pragma unroll
           for (int qt = 0; qt < NQ; ++qt) {
             uint64_t v = row_node[qt] >= 0 ? head_bits : 0ull;
-            if (tree_tile) v &= maskw[((wave + NW * qt) * 16 + n16) * 4 + (t - c.n_ptiles)];
+            if (tree_t >= 0) v &= s_mask[(wave + NW * qt) * 16 + n16][tree_t];
             const uint64_t bits = v >> (4 * grp);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -813,42 +872,140 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_wide_kernel(AttnDev a) {
     }
   };
 
+  for (int64_t x = lo; x < hi;) {
+    // ---- a piece of unit `cur`: [x, pend)
+    const int64_t pend = min(hi, cur.base + (int64_t)cur.ntl);
+    const bool whole = x == cur.base && pend == cur.base + cur.ntl;
+    const int g = cur.j / a.nqb, qb = cur.j % a.nqb;
+    const int r0 = qb * a.qb_rows;
+    int nlive = 0;
 #pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (st < n_tiles) issue_tile(st, st);
-  if (QMAX >= 2 && nlive == 2) run(std::integral_constant<int, (QMAX >= 2 ? 2 : 1)>{});
-  else if (nlive == 1) run(std::integral_constant<int, 1>{});
-  else run(std::integral_constant<int, 0>{});
-
-  // ---- epilogue: lane holds O^T[d = dt*16 + 4*grp + e][query n16]
-  const bool direct = c.ns_b == 1;
+    for (int qt = 0; qt < 2; ++qt) {
+      const int lt = wave + NW * qt;
+      const bool live = lt < tpb && r0 + lt * 16 < a.R;
+      nlive += live ? 1 : 0;
+      const int r = r0 + lt * 16 + n16;
+      const bool ok = live && r < a.R;
+      row_node[qt] = ok ? r % a.T : -1;
+      row_head[qt] = ok ? g * a.G + r / a.T : 0;
+      const uint16_t* qrow = q + (((int64_t)cur.b * a.T + (ok ? row_node[qt] : 0)) * a.Hq + row_head[qt]) * D;
 #pragma unroll
-  for (int qt = 0; qt < QMAX; ++qt) {
-    if (!tile_live[qt] || row_node[qt] < 0) continue;
-    const float lt = lacc[qt][0];
-    const int r = r0 + (wave + NW * qt) * 16 + n16;
-    if (direct) {
-      const float inv = 1.0f / lt;
-      __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)c.b * a.T + row_node[qt]) * a.Hq + row_head[qt]) * D;
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ok) {
+          qf[qt][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + grp * 8);
+        } else {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[qt][dt][e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * grp) = v;
+          for (int e = 0; e < 8; ++e) qf[qt][ks][e] = (__bf16)0.0f;
+        }
+        settle(qf[qt][ks]);
       }
-    } else {
-      const int64_t pr = ((bg * a.ns + c.split) * a.R + r);
-      float* po = a.ws_o + pr * D;
+      if (live) {
+        const uint64_t* mr = a.mask + ((int64_t)cur.b * a.T + (ok ? row_node[qt] : 0)) * a.W;
+        for (int w = 0; w < a.W; ++w) s_mask[lt * 16 + n16][w] = ok ? mr[w] : 0ull;
+      }
+      m_ref[qt] = row_node[qt] >= 0 ? kNegInf : 0.0f;
+      lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[qt][dt];
-      if (grp == 0) {
-        a.ws_ml[pr * 2 + 0] = m_ref[qt];
-        a.ws_ml[pr * 2 + 1] = lt;
+      for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    nlive = __builtin_amdgcn_readfirstlane(nlive);
+    if (x == cur.base && cur.j == 0 && tid == 0 && a.seq_status) a.seq_status[cur.b] = SVT_OK;
+
+    if (nlive == 2) run_piece(std::integral_constant<int, 2>{}, x, pend);
+    else if (nlive == 1) run_piece(std::integral_constant<int, 1>{}, x, pend);
+    else run_piece(std::integral_constant<int, 0>{}, x, pend);
+
+    // ---- end of the piece; lane holds O^T[d = dt*16 + 4*grp + e][query n16]
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      if (qt >= nlive || row_node[qt] < 0) continue;
+      const int lt = wave + NW * qt;
+      if (whole) {
+        const float inv = 1.0f / lacc[qt][0];
+        __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)cur.b * a.T + row_node[qt]) * a.Hq + row_head[qt]) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[qt][dt][e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * grp) = v;
+        }
+      } else {
+        const int slot = 2 * c + (pend == hi ? 1 : 0);
+        const int64_t pr = (int64_t)slot * a.qb_rows + lt * 16 + n16;
+        float* po = a.ws_o + pr * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[qt][dt];
+        if (grp == 0) {
+          a.ws_ml[pr * 2 + 0] = m_ref[qt];
+          a.ws_ml[pr * 2 + 1] = lacc[qt][0];
+        }
       }
     }
+    x = pend;
+    if (x < hi) advance(cur);
   }
+
+  // ---- skipped sequences: zero output rows and report why (ranges share the work)
+  for (int b = c; b < B; b += G) {
+    if (s_pref[b + 1] != s_pref[b]) continue;
+    int code;
+    stream_seq_tiles(a, b, lmax, &code);
+    __bf16* out = static_cast<__bf16*>(a.out) + (int64_t)b * a.T * a.Hq * D;
+    for (int i = tid; i < a.T * a.Hq * D; i += NT) out[i] = (__bf16)0.0f;
+    if (tid == 0 && a.seq_status) a.seq_status[b] = code;
+  }
+}
+
+// Merges the partials of the units that range ends cut, in stream order.
+// Grid (unit, group of 8 rows); 32 threads per row, four dims each.  Units
+// inside a single range return at once.
+template <int D>
+__global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
+  const int u = blockIdx.x;
+  const int qb = u % a.nqb, bg = u / a.nqb;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int* pref = a.ws_pref;
+  const int ntl = pref[b + 1] - pref[b];
+  if (ntl == 0) return;
+  const int UPB = a.Hkv * a.nqb;
+  const int64_t N = (int64_t)UPB * pref[a.B];
+  const int G = a.stream_grid;
+  const int64_t P = (int64_t)UPB * pref[b] + (int64_t)(g * a.nqb + qb) * ntl;
+  const int64_t E = P + ntl;
+  const int c0 = stream_range_of(P, N, G), c1 = stream_range_of(E - 1, N, G);
+  if (c0 == c1) return;
+  const int rl = blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int d4 = (threadIdx.x & 31) * 4;
+  const int r = qb * a.qb_rows + rl;
+  if (rl >= a.qb_rows || r >= a.R || d4 >= D) return;
+  // Online merge in range order (deterministic); ranges between c0 and c1
+  // may be empty (fewer tiles than workgroups) and hold no piece.
+  float mx = kNegInf, l = 0.0f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int cc = c0; cc <= c1; ++cc) {
+    const int64_t hi_c = stream_lo(cc + 1, N, G);
+    if (stream_lo(cc, N, G) == hi_c) continue;
+    const int slot = 2 * cc + ((cc < c1 || E == hi_c) ? 1 : 0);
+    const int64_t pr = (int64_t)slot * a.qb_rows + rl;
+    const float mi = a.ws_ml[pr * 2], li = a.ws_ml[pr * 2 + 1];
+    const f32x4 oi = *reinterpret_cast<const f32x4*>(a.ws_o + pr * D + d4);
+    if (mi == kNegInf) continue;  // no key of this piece is visible to the row
+    const float mn = fmaxf(mx, mi);
+    const float s0 = exp2f(mx - mn), s1 = exp2f(mi - mn);
+    l = l * s0 + li * s1;
+    acc = acc * s0 + oi * s1;
+    mx = mn;
+  }
+  const float inv = 1.0f / l;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[e] * inv);
+  __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
+  *reinterpret_cast<bf16x4*>(orow + d4) = v;
 }
 
 // --------------------------------------------------------------------------
@@ -1011,43 +1168,66 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
 // --------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   if (!a || a->B < 0 || a->M < 0 || a->M >= SVT_MAX_T || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0 ||
       (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16) || a->cap < 0 ||
+      a->form < SVT_ATTN_AUTO || a->form > SVT_ATTN_STREAM ||
       a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap)
     return false;
   p->T = a->M + 1;
   p->G = a->Hq / a->Hkv;
   p->R = p->G * p->T;
   p->nqt = (p->R + 15) / 16;
-  if (a->dtype == SVT_BF16) {
-    // One or two query tiles: two waves share the rows and split every key
-    // tile.  Otherwise one query tile per wave.  Two-stage rings let two
-    // workgroups share a CU, which hides more latency than a deeper ring.
-    // One query tile per wave, four waves per block; with one or two query
-    // tiles the two waves of a pair split every key tile instead.  (Measured
-    // on the five workloads: deeper rings, more tiles per wave and three-wave
-    // blocks were all slower, because they cost occupancy.)
-    if (p->nqt <= 2) {
-      p->wide = 0;
-      p->nw = 4;
-      p->qw = 1;
-      p->nwk = 2;
-      p->stages = 2;
-      p->qb_rows = (p->nw / p->nwk) * p->qw * 16;
-    } else {
-      // Wide form: up to 16 query tiles per workgroup, spread evenly over the
-      // fewest workgroups per KV head; four waves for up to four tiles, else
-      // eight (two per SIMD) with one or two tiles each.
-      const int nqb = (p->nqt + 15) / 16;
-      const int tpb = (p->nqt + nqb - 1) / nqb;
-      p->wide = 1;
-      p->nw = tpb <= 4 ? 4 : 8;
-      p->qw = (tpb + p->nw - 1) / p->nw;
-      p->nwk = 1;
-      p->stages = 4;
-      p->qb_rows = tpb * 16;
-    }
+  p->grid = 0;
+  // Key tiles the stream form would hold at most (host bound).
+  const int64_t stream_tiles = (int64_t)a->B * a->Hkv * ((p->nqt + 11) / 12) *
+                               (((int64_t)a->lmax_bound + KT - 1) / KT + (p->T + KT - 1) / KT);
+  const int cus = a->dtype == SVT_BF16 ? device_cu_count() : 0;
+  const bool stream_ok = p->nqt >= 3 && a->B <= kStreamMaxB;
+  bool use_stream = stream_ok && stream_tiles >= 8 * (int64_t)cus;
+  if (a->form == SVT_ATTN_SPLIT) use_stream = false;
+  if (a->form == SVT_ATTN_STREAM) {
+    if (a->dtype != SVT_BF16 || !stream_ok) return false;
+    use_stream = true;
+  }
+  if (a->dtype == SVT_BF16 && !use_stream) {
+    // One or two query tiles, very many sequences, or a stream too short to
+    // give every CU eight tiles: the split form, four waves per workgroup;
+    // with one or two query tiles two waves share the rows and split every
+    // key tile.
+    p->wide = 0;
+    p->nw = 4;
+    p->qw = 1;
+    p->nwk = p->nqt <= 2 ? 2 : 1;
+    p->stages = 2;
+    p->qb_rows = (p->nw / p->nwk) * p->qw * 16;
+  } else if (a->dtype == SVT_BF16) {
+    // Stream form: up to 12 query tiles per unit, spread evenly over the
+    // fewest units per KV head, two tiles per wave (each K or V fragment read
+    // from LDS feeds two MFMAs); one workgroup per CU.
+    const int nqb = (p->nqt + 11) / 12;
+    const int tpb = (p->nqt + nqb - 1) / nqb;
+    p->wide = 1;
+    p->nw = (tpb + 1) / 2;
+    p->qw = 2;
+    p->nwk = 1;
+    p->stages = 4;
+    p->qb_rows = tpb * 16;
+    // One workgroup per CU.
+    if (cus <= 0) return false;
+    p->grid = cus;
   } else {
     p->wide = 0;
     p->nwk = 1;
@@ -1057,14 +1237,22 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->qb_rows = 64;
   }
   p->nqb = (p->R + p->qb_rows - 1) / p->qb_rows;
-  // Prefix split size: enough workgroups to cover the chip several times over,
-  // fewer when the workgroups are heavy (their partials cost more).
+  if (p->wide) {
+    // Partials: two slots of qb_rows rows per workgroup, plus the prefix of
+    // tiles per sequence.
+    p->kc = 0;
+    p->ns = 1;
+    const size_t rows = (size_t)2 * p->grid * p->qb_rows;
+    const size_t pref_bytes = (((size_t)a->B + 1) * sizeof(int) + 255) / 256 * 256;
+    p->ws_bytes = pref_bytes + rows * (a->D + 2) * sizeof(float);
+    return true;
+  }
+  // Prefix split size: enough workgroups to cover the chip several times over.
   const int64_t ptiles = ((int64_t)a->lmax_bound + KT - 1) / KT;
   const int64_t units = ptiles * a->B * a->Hkv * p->nqb;
-  const int64_t target = p->wide ? 1536 : 1024;
-  const int64_t min_tiles = p->wide ? 8 : 4;
+  const int64_t target = 1024;
   int64_t tiles_per_split = (units + target - 1) / target;
-  if (tiles_per_split < min_tiles) tiles_per_split = min_tiles;
+  if (tiles_per_split < 4) tiles_per_split = 4;
   p->kc = (int)(tiles_per_split * KT);
   p->ns = a->lmax_bound > 0 ? (int)((a->lmax_bound + p->kc - 1) / p->kc) : 1;
   if (p->ns < 1) p->ns = 1;
@@ -1085,10 +1273,20 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.status = a->status;
   d.out = a->out;
   d.seq_status = a->seq_status;
-  float* ws = static_cast<float*>(a->workspace);
-  const size_t n_o = p.ns > 1 ? (size_t)a->B * a->Hkv * p.ns * p.R * a->D : 0;
-  d.ws_o = ws;
-  d.ws_ml = ws ? ws + n_o : nullptr;
+  if (p.wide) {
+    unsigned char* w = static_cast<unsigned char*>(a->workspace);
+    const size_t pref_bytes = (((size_t)a->B + 1) * sizeof(int) + 255) / 256 * 256;
+    d.ws_pref = reinterpret_cast<int*>(w);
+    d.ws_o = reinterpret_cast<float*>(w + pref_bytes);
+    d.ws_ml = d.ws_o + (size_t)2 * p.grid * p.qb_rows * a->D;
+  } else {
+    float* ws = static_cast<float*>(a->workspace);
+    const size_t n_o = p.ns > 1 ? (size_t)a->B * a->Hkv * p.ns * p.R * a->D : 0;
+    d.ws_pref = nullptr;
+    d.ws_o = ws;
+    d.ws_ml = ws ? ws + n_o : nullptr;
+  }
+  d.stream_grid = p.grid;
   d.cap = a->cap;
   d.B = a->B;
   d.T = p.T;
@@ -1104,6 +1302,27 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.qb_rows = p.qb_rows;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   d.scale_log2 = scale * kLog2e;
+  if (p.wide) {
+    const dim3 g(p.grid);
+#define SVT_STREAM(DD)                                                                                 \
+  switch (p.nw) {                                                                                      \
+    case 2: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 2>), g, dim3(128), 0, s, d); break;          \
+    case 3: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 3>), g, dim3(192), 0, s, d); break;          \
+    case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4>), g, dim3(256), 0, s, d); break;          \
+    case 5: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 5>), g, dim3(320), 0, s, d); break;          \
+    default: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6>), g, dim3(384), 0, s, d); break;         \
+  }
+    if (a->D == 128) { SVT_STREAM(128) } else { SVT_STREAM(64) }
+#undef SVT_STREAM
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nu = (int64_t)a->B * a->Hkv * p.nqb;
+    if (nu > 0x7FFFFFF0) return hipErrorInvalidValue;
+    const dim3 cg((unsigned)nu, (unsigned)((p.qb_rows + 7) / 8));
+    if (a->D == 128) hipLaunchKernelGGL((attn_stream_combine_kernel<128>), cg, dim3(256), 0, s, d);
+    else hipLaunchKernelGGL((attn_stream_combine_kernel<64>), cg, dim3(256), 0, s, d);
+    return hipGetLastError();
+  }
   const int64_t nunits = (int64_t)a->B * a->Hkv * p.ns;
   if (nunits == 0) return hipSuccess;
   const int64_t nwg = 8 * p.nqb * ((nunits + 7) / 8);
@@ -1115,18 +1334,11 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
 #define SVT_ATTN_BF16(DD, QQ, SS, WW) \
   hipLaunchKernelGGL((attn_bf16_kernel<DD, QQ, SS, WW>), dim3(grid), dim3(WW * 64), 0, s, d)
 #define SVT_ATTN_BF16_QW(DD, SS, WW) SVT_ATTN_BF16(DD, 1, SS, WW);
-#define SVT_ATTN_WIDE(DD)                                                                             \
-  if (p.nw == 4) hipLaunchKernelGGL((attn_bf16_wide_kernel<DD, 4, 1>), dim3(grid), dim3(256), 0, s, d);   \
-  else if (p.qw == 1) hipLaunchKernelGGL((attn_bf16_wide_kernel<DD, 8, 1>), dim3(grid), dim3(512), 0, s, d); \
-  else hipLaunchKernelGGL((attn_bf16_wide_kernel<DD, 8, 2>), dim3(grid), dim3(512), 0, s, d);
-    if (p.wide) {
-      if (a->D == 128) { SVT_ATTN_WIDE(128) } else { SVT_ATTN_WIDE(64) }
-    } else if (a->D == 128) {
+    if (a->D == 128) {
       SVT_ATTN_BF16_QW(128, 2, 4)
     } else {
       SVT_ATTN_BF16_QW(64, 2, 4)
     }
-#undef SVT_ATTN_WIDE
 #undef SVT_ATTN_BF16_QW
 #undef SVT_ATTN_BF16
   } else {

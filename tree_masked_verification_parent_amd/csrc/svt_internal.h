@@ -17,7 +17,8 @@ constexpr int kWave = 64;
 struct AttnPlan {
   int T, G, R;       // tree rows, query heads per KV head, query rows per KV head (G*T)
   int nqt;           // 16-row query tiles per KV head
-  int wide;          // bf16: 1 = wide kernel (two tiles per wave, 4-deep ring)
+  int wide;          // bf16: 1 = stream form (one workgroup per CU over the tile stream)
+  int grid;          // stream form: workgroups (compute units)
   int qw;            // query tiles per wave (bf16 path)
   int stages;        // LDS ring depth, 2 or 4 (bf16 path)
   int nw;            // waves per workgroup (bf16 path)

@@ -30,6 +30,7 @@ SVT_ERR_LENGTH = -9
 SVT_FP32 = 0
 SVT_BF16 = 1
 SVT_SYNC_CHECK = 1
+SVT_ATTN_AUTO, SVT_ATTN_SPLIT, SVT_ATTN_STREAM = 0, 1, 2
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -41,7 +42,7 @@ class AttnArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("q", _P), ("k_cache", _P), ("v_cache", _P), ("cap", _I64),
                 ("len", _P), ("lmax", _P), ("lmax_bound", _I32), ("k_tree", _P), ("v_tree", _P), ("mask", _P),
                 ("status", _P), ("out", _P), ("seq_status", _P), ("workspace", _P),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("form", _I32)]
 
 
 class AcceptArgs(ctypes.Structure):
@@ -132,7 +133,7 @@ def _dtype_code(t):
 
 
 def attn_args(q, k_cache, v_cache, lens, lmax, lmax_bound: int, k_tree, v_tree, mask, out, status=None,
-              seq_status=None, scale: float = 0.0, workspace=None) -> AttnArgs:
+              seq_status=None, scale: float = 0.0, workspace=None, form: int = 0) -> AttnArgs:
     B, T, Hq, D = q.shape
     a = AttnArgs()
     a.B, a.M, a.Hq, a.Hkv, a.D = B, T - 1, Hq, k_cache.shape[1], D
@@ -145,6 +146,7 @@ def attn_args(q, k_cache, v_cache, lens, lmax, lmax_bound: int, k_tree, v_tree, 
     a.status, a.out, a.seq_status = _ptr(status), _ptr(out), _ptr(seq_status)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.form = int(form)
     return a
 
 
