@@ -798,18 +798,19 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
           for (int ks = 0; ks < NKS; ++ks)
             kf[u][ks] = *reinterpret_cast<const bf16x8*>(kl + 16 * u * TL::ROWB + koff[ks]);
         __builtin_amdgcn_sched_barrier(0);
+        // Scores tile by tile (query tile 0 first), so the VALU work on tile
+        // 0's scores can overlap the MFMAs of tile 1.
         f32x4 sacc[NQ][4];
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt)
+        for (int qt = 0; qt < NQ; ++qt) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) sacc[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+          for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int qt = 0; qt < NQ; ++qt)
+            for (int u = 0; u < 4; ++u)
               sacc[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], sacc[qt][u], 0, 0, 0);
+        }
         // sacc[qt][u][e] = score of key 16u + 4*grp + e of the tile for query n16.
         if (tree_t >= 0 || nvalid < KT) {  // wave-uniform, rare
           const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
@@ -825,30 +826,33 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
                 if (!((bits >> (16 * u + e)) & 1ull)) sacc[qt][u][e] = kNegInf;
           }
         }
-        bf16x8 pf[NQ][2];
+        float mx[NQ];
+        bool up = false;
 #pragma unroll
         for (int qt = 0; qt < NQ; ++qt) {
-          float mx = sacc[qt][0][0];
+          float m = sacc[qt][0][0];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[qt][u][e]);
-          mx *= sc;
-          if (__any(mx > m_ref[qt] + kRescale)) {
-            const float m_new = fmaxf(m_ref[qt], group_max(mx));
-            const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
-            lacc[qt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
-            m_ref[qt] = m_new;
-          }
-          const float neg_m = m_ref[qt] == kNegInf ? 0.0f : -m_ref[qt];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pf[qt][h][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qt][2 * h + e / 4][e % 4], sc, neg_m));
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, sacc[qt][u][e]);
+          mx[qt] = m * sc;
+          up = up || (mx[qt] > m_ref[qt] + kRescale);
         }
+        if (__any(up)) {  // one wave-uniform branch per key tile; first tiles, then rare
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt) {
+            const float m_new = fmaxf(m_ref[qt], group_max(mx[qt]));
+            if (m_new > m_ref[qt] + kRescale || m_ref[qt] == kNegInf) {
+              const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+              lacc[qt] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+              m_ref[qt] = m_new;
+            }
+          }
+        }
+        // P V per query tile and 32-key half; the exponentials of the next
+        // (tile, half) can overlap the MFMAs of the current one.
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const unsigned char* vh = vl + 32 * h * TL::ROWB;
@@ -860,13 +864,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
             vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
           }
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
+          for (int qt = 0; qt < NQ; ++qt) {
+            const float neg_m = m_ref[qt] == kNegInf ? 0.0f : -m_ref[qt];
+            bf16x8 pf;
 #pragma unroll
-            for (int qt = 0; qt < NQ; ++qt)
-              o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[qt][h], o[qt][dt], 0, 0, 0);
+            for (int e = 0; e < 8; ++e)
+              pf[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qt][2 * h + e / 4][e % 4], sc, neg_m));
 #pragma unroll
-          for (int qt = 0; qt < NQ; ++qt)
-            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qt][h], lacc[qt], 0, 0, 0);
+            for (int dt = 0; dt < NDT; ++dt)
+              o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[qt][dt], 0, 0, 0);
+            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc[qt], 0, 0, 0);
+          }
         }
       }
     }
