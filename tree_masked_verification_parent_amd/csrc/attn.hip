@@ -599,7 +599,7 @@ __device__ __forceinline__ int64_t stream_lo(int64_t c, int64_t n, int g) { retu
 // Range holding stream tile x.
 __device__ __forceinline__ int stream_range_of(int64_t x, int64_t n, int g) { return (int)(((x + 1) * g - 1) / n); }
 
-template <int D, int NW>
+template <int D, int NW, int QMAX>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
   constexpr int kStages = 4;
   constexpr int NKS = D / 32;
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
   __shared__ int s_len[kStreamMaxB];
   __shared__ int s_wsum[NW];
   __shared__ int s_carry;
-  __shared__ uint64_t s_mask[NW * 2 * 16][4];  // each lane's tree-mask words, its own rows only
+  __shared__ uint64_t s_mask[NW * QMAX * 16][4];  // each lane's tree-mask words, its own rows only
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -660,11 +660,30 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
   if (c == 0 && a.ws_pref)
     for (int b = tid; b <= B; b += NT) a.ws_pref[b] = s_pref[b];
 
-  // Cursor over the stream: unit (b, j = g*nqb + qb), its first tile `base`
-  // and its tile count.  All fields are wave-uniform.
+  const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.kcache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.vcache);
+  const uint16_t* __restrict__ ktr = static_cast<const uint16_t*>(a.ktree);
+  const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
+  const int tpb = a.qb_rows / 16;
+
+  // Cursor over the stream: unit (b, j = g*nqb + qb), its first tile `base`,
+  // its tile count, and what the per-tile source addresses need (content
+  // length, prefix tiles, base pointers), refreshed only when the cursor
+  // enters a unit.  All fields are wave-uniform.
   struct Cur {
-    int b, j, ntl;
+    int b, j, ntl, L, np;
     int64_t base;
+    const uint16_t *kp, *vp, *kt, *vt;  // prefix content start, tree rows
+  };
+  auto fill = [&](Cur& r) {
+    r.L = __builtin_amdgcn_readfirstlane(s_len[r.b]);
+    r.np = (r.L + KT - 1) / KT;
+    const int64_t bg = (int64_t)r.b * a.Hkv + r.j / a.nqb;
+    r.kp = kc + (bg * a.cap + (lmax - r.L)) * D;
+    r.vp = vc + (bg * a.cap + (lmax - r.L)) * D;
+    r.kt = ktr + bg * a.T * D;
+    r.vt = vtr + bg * a.T * D;
   };
   auto locate = [&](int64_t x) {
     int l = 0, h = B;
@@ -679,6 +698,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     const int64_t sb = (int64_t)UPB * s_pref[r.b];
     r.j = (int)((x - sb) / r.ntl);
     r.base = sb + (int64_t)r.j * r.ntl;
+    fill(r);
     return r;
   };
   auto advance = [&](Cur& r) {
@@ -690,49 +710,59 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
       } while (r.b < B && s_pref[r.b + 1] == s_pref[r.b]);
       r.ntl = r.b < B ? __builtin_amdgcn_readfirstlane(s_pref[r.b + 1] - s_pref[r.b]) : 0;
     }
+    if (r.b < B) fill(r);
   };
-
-  const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.kcache);
-  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.vcache);
-  const uint16_t* __restrict__ ktr = static_cast<const uint16_t*>(a.ktree);
-  const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
-  const int tpb = a.qb_rows / 16;
 
   // Source rows of stream tile x of unit `r`; tree_t = -1 for a prefix tile.
   auto tile_src = [&](const Cur& r, int64_t x, const uint16_t*& kb, const uint16_t*& vb, int& nvalid, int& tree_t) {
     const int t = (int)(x - r.base);
-    const int L = s_len[r.b];
-    const int np = (L + KT - 1) / KT;
-    const int64_t bg = (int64_t)r.b * a.Hkv + r.j / a.nqb;
-    if (t < np) {
-      const int64_t col = (int64_t)(lmax - L) + (int64_t)t * KT;
-      kb = kc + (bg * a.cap + col) * D;
-      vb = vc + (bg * a.cap + col) * D;
-      nvalid = min(KT, L - t * KT);
+    if (t < r.np) {
+      kb = r.kp + (int64_t)t * (KT * D);
+      vb = r.vp + (int64_t)t * (KT * D);
+      nvalid = min(KT, r.L - t * KT);
       tree_t = -1;
     } else {
-      const int j0 = (t - np) * KT;
-      kb = ktr + (bg * a.T + j0) * D;
-      vb = vtr + (bg * a.T + j0) * D;
+      const int j0 = (t - r.np) * KT;
+      kb = r.kt + (int64_t)j0 * D;
+      vb = r.vt + (int64_t)j0 * D;
       nvalid = min(KT, a.T - j0);
-      tree_t = t - np;
+      tree_t = t - r.np;
     }
   };
+  // Lane-constant element offsets of this wave's copies for a full tile.
+  int cofk[TL::PER_WAVE], cofv[TL::PER_WAVE];
+#pragma unroll
+  for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
+    const int ins = (wave + NW * jj) % TL::NINSTR;
+    const int row = ins * TL::RPI + lane / TL::CPR;
+    const int slot = lane % TL::CPR;
+    cofk[jj] = row * D + 8 * (slot ^ TL::swz_k(row));
+    cofv[jj] = row * D + 8 * (slot ^ TL::swz_v(row));
+  }
   auto issue_tile = [&](const Cur& r, int64_t x, int st) {
     const uint16_t *kb, *vb;
     int nvalid, tree_t;
     tile_src(r, x, kb, vb, nvalid, tree_t);
     unsigned char* kl = lds + st * TL::STAGEB;
     unsigned char* vl = kl + TL::TILEB;
+    if (nvalid == KT) {
 #pragma unroll
-    for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
-      const int ins = (wave + NW * jj) % TL::NINSTR;
-      const int row = ins * TL::RPI + lane / TL::CPR;
-      const int slot = lane % TL::CPR;
-      const int src = (nvalid == KT ? row : min(row, nvalid - 1)) * D;
-      copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
-      copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
+      for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
+        const int ins = (wave + NW * jj) % TL::NINSTR;
+        copy16_to_lds(kb + cofk[jj], kl + ins * 1024);
+        copy16_to_lds(vb + cofv[jj], vl + ins * 1024);
+      }
+    } else {
+      // Rows past the valid ones repeat the last valid row; they are masked.
+#pragma unroll
+      for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
+        const int ins = (wave + NW * jj) % TL::NINSTR;
+        const int row = ins * TL::RPI + lane / TL::CPR;
+        const int slot = lane % TL::CPR;
+        const int src = min(row, nvalid - 1) * D;
+        copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
+        copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
+      }
     }
   };
 
@@ -750,132 +780,157 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   const float sc = a.scale_log2;
 
-  // Per-piece state of this wave's query tiles (block tiles wave, wave + NW).
-  bf16x8 qf[2][NKS];
-  f32x4 o[2][NDT];
-  f32x4 lacc[2];
-  float m_ref[2];
-  int row_node[2], row_head[2];
+  // Per-piece state of this wave's query tiles (block tiles wave, wave + NW, ...).
+  bf16x8 qf[QMAX][NKS];
+  f32x4 o[QMAX][NDT];
+  f32x4 lacc[QMAX];
+  float m_ref[QMAX];
+  int row_node[QMAX], row_head[QMAX];
 
-  Cur cur{0, 0, 0, 0}, pcur{0, 0, 0, 0};
+  Cur cur{}, pcur{};
   if (lo < hi) {
     cur = locate(lo);
     pcur = cur;
   }
-  // Producer: a cursor kStages - 1 tiles ahead of the consumer.
+  // Producer: a cursor that issues the copies of stream tile y + 2 once tile
+  // y is visible.  landed(y): wait until tile y's copies are done (only tile
+  // y + 1 may still be in flight), barrier, then issue tile y + 2 into the
+  // stage that tile y - 2 used (every wave has finished with it: its P V ran
+  // before this barrier).  While a wave works on tiles y - 1 (P V) and y
+  // (scores), tiles y + 1 and y + 2 are in flight: four stages.
   int64_t px = lo;
   auto produce = [&](int st) {
     if (px == pcur.base + pcur.ntl) advance(pcur);
     issue_tile(pcur, px, st);
     ++px;
   };
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (lo + st < hi) produce(st);
+  if (lo < hi) produce(0);
+  if (lo + 1 < hi) produce(1);
+  auto landed = [&](int64_t y) {
+    if (y + 1 < hi) wait_vmcnt<TL::LOADS>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (y + 2 < hi) produce((int)((y - lo + 2) % kStages));
+  };
 
-  // The tile loop of one piece, for a wave with NQ live query tiles.  Each
-  // piece runs one instance, so the accumulators keep their registers.
-  auto run_piece = [&](auto nq_c, int64_t x0, int64_t x1) {
+  // Scores of stream tile y for NQ query tiles: s[qt][u][e] = score of key
+  // 16u + 4*grp + e of the tile for query n16.
+  auto scores = [&](auto nq_c, int64_t y, f32x4 (&sacc)[decltype(nq_c)::value][4]) {
     constexpr int NQ = decltype(nq_c)::value;
-    for (int64_t x = x0; x < x1; ++x) {
-      const int64_t rem = hi - 1 - x;
-      if (rem >= 2) wait_vmcnt<2 * TL::LOADS>();
-      else if (rem == 1) wait_vmcnt<TL::LOADS>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (x + kStages - 1 < hi) produce((int)((x - lo + kStages - 1) % kStages));
-      if constexpr (NQ > 0) {
-        const uint16_t *kb_, *vb_;
-        int nvalid, tree_t;
-        tile_src(cur, x, kb_, vb_, nvalid, tree_t);
-        const unsigned char* kl = lds + ((x - lo) % kStages) * TL::STAGEB;
-        const unsigned char* vl = kl + TL::TILEB;
-        // All K fragments of the tile are requested before the first score MFMA.
-        bf16x8 kf[4][NKS];
+    const unsigned char* kl = lds + ((y - lo) % kStages) * TL::STAGEB;
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sacc[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          sacc[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8*>(kl + 16 * u * TL::ROWB + koff[ks]), qf[qt][ks], sacc[qt][u], 0, 0, 0);
+    }
+  };
+  // Mask, softmax and P V of stream tile y from its scores.
+  auto finish = [&](auto nq_c, int64_t y, f32x4 (&sacc)[decltype(nq_c)::value][4]) {
+    constexpr int NQ = decltype(nq_c)::value;
+    const uint16_t *kb_, *vb_;
+    int nvalid, tree_t;
+    tile_src(cur, y, kb_, vb_, nvalid, tree_t);
+    const unsigned char* vl = lds + ((y - lo) % kStages) * TL::STAGEB + TL::TILEB;
+    if (tree_t >= 0 || nvalid < KT) {  // wave-uniform, rare
+      const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt) {
+        uint64_t v = row_node[qt] >= 0 ? head_bits : 0ull;
+        if (tree_t >= 0) v &= s_mask[(wave + NW * qt) * 16 + n16][tree_t];
+        const uint64_t bits = v >> (4 * grp);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            kf[u][ks] = *reinterpret_cast<const bf16x8*>(kl + 16 * u * TL::ROWB + koff[ks]);
-        __builtin_amdgcn_sched_barrier(0);
-        // Scores tile by tile (query tile 0 first), so the VALU work on tile
-        // 0's scores can overlap the MFMAs of tile 1.
-        f32x4 sacc[NQ][4];
+          for (int e = 0; e < 4; ++e)
+            if (!((bits >> (16 * u + e)) & 1ull)) sacc[qt][u][e] = kNegInf;
+      }
+    }
+    float mx[NQ];
+    bool up = false;
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) {
+    for (int qt = 0; qt < NQ; ++qt) {
+      float m = sacc[qt][0][0];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) sacc[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, sacc[qt][u][e]);
+      mx[qt] = m * sc;
+      up = up || (mx[qt] > m_ref[qt] + kRescale);
+    }
+    if (__any(up)) {  // one wave-uniform branch per key tile; first tiles, then rare
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-              sacc[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][ks], qf[qt][ks], sacc[qt][u], 0, 0, 0);
+      for (int qt = 0; qt < NQ; ++qt) {
+        const float m_new = fmaxf(m_ref[qt], group_max(mx[qt]));
+        if (m_new > m_ref[qt] + kRescale || m_ref[qt] == kNegInf) {
+          const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+          lacc[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+          m_ref[qt] = m_new;
         }
-        // sacc[qt][u][e] = score of key 16u + 4*grp + e of the tile for query n16.
-        if (tree_t >= 0 || nvalid < KT) {  // wave-uniform, rare
-          const uint64_t head_bits = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+      }
+    }
 #pragma unroll
-          for (int qt = 0; qt < NQ; ++qt) {
-            uint64_t v = row_node[qt] >= 0 ? head_bits : 0ull;
-            if (tree_t >= 0) v &= s_mask[(wave + NW * qt) * 16 + n16][tree_t];
-            const uint64_t bits = v >> (4 * grp);
+    for (int h = 0; h < 2; ++h) {
+      const unsigned char* vh = vl + 32 * h * TL::ROWB;
+      bf16x8 vf[NDT];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+      for (int dt = 0; dt < NDT; ++dt) {
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + voff[dt]));
+        const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + 16 * TL::ROWB + voff[dt]));
+        vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (!((bits >> (16 * u + e)) & 1ull)) sacc[qt][u][e] = kNegInf;
-          }
-        }
-        float mx[NQ];
-        bool up = false;
+      for (int qt = 0; qt < NQ; ++qt) {
+        const float neg_m = m_ref[qt] == kNegInf ? 0.0f : -m_ref[qt];
+        bf16x8 pf;
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) {
-          float m = sacc[qt][0][0];
+        for (int e = 0; e < 8; ++e)
+          pf[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qt][2 * h + e / 4][e % 4], sc, neg_m));
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, sacc[qt][u][e]);
-          mx[qt] = m * sc;
-          up = up || (mx[qt] > m_ref[qt] + kRescale);
-        }
-        if (__any(up)) {  // one wave-uniform branch per key tile; first tiles, then rare
-#pragma unroll
-          for (int qt = 0; qt < NQ; ++qt) {
-            const float m_new = fmaxf(m_ref[qt], group_max(mx[qt]));
-            if (m_new > m_ref[qt] + kRescale || m_ref[qt] == kNegInf) {
-              const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
-              lacc[qt] *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
-              m_ref[qt] = m_new;
-            }
-          }
-        }
-        // P V per query tile and 32-key half; the exponentials of the next
-        // (tile, half) can overlap the MFMAs of the current one.
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const unsigned char* vh = vl + 32 * h * TL::ROWB;
-          bf16x8 vf[NDT];
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + voff[dt]));
-            const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + 16 * TL::ROWB + voff[dt]));
-            vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-#pragma unroll
-          for (int qt = 0; qt < NQ; ++qt) {
-            const float neg_m = m_ref[qt] == kNegInf ? 0.0f : -m_ref[qt];
-            bf16x8 pf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pf[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qt][2 * h + e / 4][e % 4], sc, neg_m));
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-              o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[qt][dt], 0, 0, 0);
-            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc[qt], 0, 0, 0);
-          }
-        }
+        for (int dt = 0; dt < NDT; ++dt)
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, o[qt][dt], 0, 0, 0);
+        lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc[qt], 0, 0, 0);
+      }
+    }
+  };
+
+  // The tiles of one piece for a wave with NQ live query tiles, software
+  // pipelined: the scores of tile x + 1 are issued before the softmax and
+  // P V of tile x, so the matrix cores have independent work while the
+  // softmax runs.  Each piece runs one instance, so the accumulators keep
+  // their registers.
+  auto run_piece = [&](auto nq_c, int64_t x0, int64_t x1) {
+    constexpr int NQ = decltype(nq_c)::value;
+    if constexpr (NQ == 0) {
+      for (int64_t x = x0; x < x1; ++x) landed(x);
+    } else {
+      f32x4 sa[NQ][4], sb[NQ][4];
+      landed(x0);
+      scores(nq_c, x0, sa);
+      int64_t x = x0;
+      while (x + 2 < x1) {
+        landed(x + 1);
+        scores(nq_c, x + 1, sb);
+        finish(nq_c, x, sa);
+        landed(x + 2);
+        scores(nq_c, x + 2, sa);
+        finish(nq_c, x + 1, sb);
+        x += 2;
+      }
+      if (x + 1 < x1) {
+        landed(x + 1);
+        scores(nq_c, x + 1, sb);
+        finish(nq_c, x, sa);
+        finish(nq_c, x + 1, sb);
+      } else {
+        finish(nq_c, x, sa);
       }
     }
   };
@@ -888,7 +943,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     const int r0 = qb * a.qb_rows;
     int nlive = 0;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QMAX; ++qt) {
       const int lt = wave + NW * qt;
       const bool live = lt < tpb && r0 + lt * 16 < a.R;
       nlive += live ? 1 : 0;
@@ -919,13 +974,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     nlive = __builtin_amdgcn_readfirstlane(nlive);
     if (x == cur.base && cur.j == 0 && tid == 0 && a.seq_status) a.seq_status[cur.b] = SVT_OK;
 
-    if (nlive == 2) run_piece(std::integral_constant<int, 2>{}, x, pend);
+    if (QMAX >= 2 && nlive == 2) run_piece(std::integral_constant<int, (QMAX >= 2 ? 2 : 1)>{}, x, pend);
     else if (nlive == 1) run_piece(std::integral_constant<int, 1>{}, x, pend);
     else run_piece(std::integral_constant<int, 0>{}, x, pend);
 
     // ---- end of the piece; lane holds O^T[d = dt*16 + 4*grp + e][query n16]
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QMAX; ++qt) {
       if (qt >= nlive || row_node[qt] < 0) continue;
       const int lt = wave + NW * qt;
       if (whole) {
@@ -1228,8 +1283,8 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     const int nqb = (p->nqt + 11) / 12;
     const int tpb = (p->nqt + nqb - 1) / nqb;
     p->wide = 1;
-    p->nw = (tpb + 1) / 2;
-    p->qw = 2;
+    p->nw = tpb <= 4 ? 4 : tpb <= 6 ? 6 : tpb <= 9 ? 9 : 12;
+    p->qw = 1;
     p->nwk = 1;
     p->stages = 4;
     p->qb_rows = tpb * 16;
@@ -1314,11 +1369,10 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     const dim3 g(p.grid);
 #define SVT_STREAM(DD)                                                                                 \
   switch (p.nw) {                                                                                      \
-    case 2: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 2>), g, dim3(128), 0, s, d); break;          \
-    case 3: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 3>), g, dim3(192), 0, s, d); break;          \
-    case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4>), g, dim3(256), 0, s, d); break;          \
-    case 5: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 5>), g, dim3(320), 0, s, d); break;          \
-    default: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6>), g, dim3(384), 0, s, d); break;         \
+    case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4, 1>), g, dim3(256), 0, s, d); break;       \
+    case 6: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6, 1>), g, dim3(384), 0, s, d); break;       \
+    case 9: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 9, 1>), g, dim3(576), 0, s, d); break;       \
+    default: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 12, 1>), g, dim3(768), 0, s, d); break;     \
   }
     if (a->D == 128) { SVT_STREAM(128) } else { SVT_STREAM(64) }
 #undef SVT_STREAM
