@@ -130,6 +130,13 @@ __device__ __forceinline__ void write_seq_status(const AttnDev& a, const WgCtx& 
   if (a.seq_status && c.split == 0 && c.qb == 0 && c.g == 0 && threadIdx.x == 0) a.seq_status[c.b] = c.code;
 }
 
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // --------------------------------------------------------------------------
 // bf16 MFMA kernel
 // --------------------------------------------------------------------------
@@ -150,8 +157,18 @@ struct Tile {
   static constexpr int STAGEB = 2 * TILEB;
   static constexpr int NINSTR = TILEB / 1024;  // 1 KB copy instructions per K or V tile
   static constexpr int PER_WAVE = (NINSTR + NW - 1) / NW;  // per wave (NW waves share a tile)
-  static constexpr int LOADS = 2 * PER_WAVE;   // copy instructions per wave per stage
   static constexpr int RPI = 1024 / ROWB;      // rows per copy instruction
+  // Copy j of wave w is block w + NW * j; when NW does not divide NINSTR the
+  // last round has fewer blocks than waves and the waves past them skip it.
+  static constexpr bool EXACT = NINSTR % NW == 0;
+  __device__ static __forceinline__ bool has_copy(int w, int j) { return EXACT || w + NW * j < NINSTR; }
+  // Waits until at most `later` tiles' copies of this wave are pending; a wave
+  // that skips the last round has 2 * (PER_WAVE - 1) copies per tile.
+  template <int LATER>
+  __device__ static __forceinline__ void wait_tiles(int w) {
+    if (has_copy(w, PER_WAVE - 1)) wait_vmcnt<2 * PER_WAVE * LATER>();
+    else wait_vmcnt<2 * (PER_WAVE - 1) * LATER>();
+  }
   __device__ static __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   __device__ static __forceinline__ int swz_v(int r) { return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1); }
 };
@@ -171,12 +188,6 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, unsigned char* lds)
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory");
 }
 
-// Wait until at most N of this wave's vector-memory operations are pending.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 // Makes the compiler complete the loads of x here.  Its wait-count pass does
 // not see the asm copies; a register loaded before the main loop and first
 // read inside it would otherwise get a vmcnt(0) wait inside the loop, which
@@ -336,11 +347,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
       nvalid = min(KT, a.T - j0);
     }
   };
-  // Copy tile t into stage `st`.  Every wave issues the same number of copy
-  // instructions (TL::LOADS), so one vmcnt value tracks a tile for all of
-  // them; when NW does not divide the count, a few 1 KB blocks are copied
-  // twice (identical bytes to the same place).  Rows past the valid ones
-  // repeat the last valid row; they are masked out.
+  // Copy tile t into stage `st`: 1 KB blocks dealt round-robin to the waves
+  // (a wave past the last block of the final round skips it and waits on
+  // its own smaller count).  Rows past the valid ones repeat the last valid
+  // row; they are masked out.
   // Per-lane source rows and swizzled chunk offsets of this wave's copies.
   int crow[TL::PER_WAVE], ck[TL::PER_WAVE], cv[TL::PER_WAVE];
 #pragma unroll
@@ -359,6 +369,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
     unsigned char* vl = kl + TL::TILEB;
 #pragma unroll
     for (int j = 0; j < TL::PER_WAVE; ++j) {
+      if (!TL::has_copy(wave, j)) continue;
       const int ins = (wave + NW * j) % TL::NINSTR;
       const int src = (nvalid == KT ? crow[j] : min(crow[j], nvalid - 1)) * D;
       copy16_to_lds(kb + src + ck[j], kl + ins * 1024);
@@ -453,8 +464,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
     // tile t has landed once at most the copies of later tiles are pending
     static_assert(kStages == 2 || kStages == 4, "wait ladder covers 2 or 4 stages");
     const int later = min(kStages - 2, n_tiles - 1 - t);
-    if (kStages == 4 && later >= 2) wait_vmcnt<2 * TL::LOADS>();
-    else if (kStages == 4 && later == 1) wait_vmcnt<TL::LOADS>();
+    if (kStages == 4 && later >= 2) TL::template wait_tiles<2>(wave);
+    else if (kStages == 4 && later == 1) TL::template wait_tiles<1>(wave);
     else wait_vmcnt<0>();
     lds_barrier();
     if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1, (t + kStages - 1) % kStages);
@@ -748,6 +759,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     if (nvalid == KT) {
 #pragma unroll
       for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
+        if (!TL::has_copy(wave, jj)) continue;
         const int ins = (wave + NW * jj) % TL::NINSTR;
         copy16_to_lds(kb + cofk[jj], kl + ins * 1024);
         copy16_to_lds(vb + cofv[jj], vl + ins * 1024);
@@ -756,6 +768,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
       // Rows past the valid ones repeat the last valid row; they are masked.
 #pragma unroll
       for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
+        if (!TL::has_copy(wave, jj)) continue;
         const int ins = (wave + NW * jj) % TL::NINSTR;
         const int row = ins * TL::RPI + lane / TL::CPR;
         const int slot = lane % TL::CPR;
@@ -807,7 +820,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
   if (lo < hi) produce(0);
   if (lo + 1 < hi) produce(1);
   auto landed = [&](int64_t y) {
-    if (y + 1 < hi) wait_vmcnt<TL::LOADS>();
+    if (y + 1 < hi) TL::template wait_tiles<1>(wave);
     else wait_vmcnt<0>();
     lds_barrier();
     if (y + 2 < hi) produce((int)((y - lo + 2) % kStages));
