@@ -52,8 +52,10 @@ def lib():
         L.oracle_argmax.restype = None
         L.oracle_accept.argtypes = [P, P, P, P, i32, i32, P, P, P]
         L.oracle_accept.restype = None
-        L.oracle_commit.argtypes = [P, P, i32, i32, i32, i64, i32, i32, P, P, P, P, P, P, P, P]
+        L.oracle_commit.argtypes = [P, P, i32, i32, i32, i64, i32, i32, P, P, P, P, P, P, P, P, i32, P, i32]
         L.oracle_commit.restype = ctypes.c_int
+        L.oracle_realign.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, i32, P, P, P]
+        L.oracle_realign.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -138,21 +140,41 @@ def accept(amax, tree_tokens, parents, M: int, status=None):
 
 
 def commit(kv_main: np.ndarray, kv_branch: np.ndarray, M: int, tokens_main, tree_tokens, lens,
-           lmax: int, path, accept_len, status=None, want_pos_ids: bool = True):
-    """kv_main [L][2][B][Hkv][cap][...] and kv_branch [L][2][B][Hkv][T][...] of
-    any dtype (raw bytes are moved).  Works on copies; returns
-    (rc, kv_main', tokens_main', lens', lmax', pos_ids)."""
+           lmax: int, path, accept_len, status=None, want_pos_ids: bool = True, mode: int = 0, slot=None):
+    """kv_main [L][2][rows][Hkv][cap][...] and kv_branch [L][2][B][Hkv][T][...] of
+    any dtype (raw bytes are moved); rows = B unless `slot` maps each sequence
+    to a pool row.  mode 0 re-pads (EQSPEC), 1 appends (EXSPEC).  Works on
+    copies; returns (rc, kv_main', tokens_main', lens', lmax', pos_ids)."""
     km = np.array(kv_main, copy=True, order="C")
     kb = _c(kv_branch, kv_branch.dtype)
-    L, _, B, Hkv, cap = km.shape[:5]
+    L, _, rows, Hkv, cap = km.shape[:5]
+    B = len(lens)
     row_bytes = km[0, 0, 0, 0, 0].nbytes if km.size else 0
     tm = None if tokens_main is None else np.array(tokens_main, dtype=np.int32, copy=True, order="C")
     tt = _c(tree_tokens, np.int32)
     ln = np.array(lens, dtype=np.int32, copy=True)
     lm = np.array([lmax], dtype=np.int32)
-    pos = np.zeros((B, cap), dtype=np.int32) if want_pos_ids else None
+    pos = np.zeros((rows, cap), dtype=np.int32) if want_pos_ids else None
     st = None if status is None else _c(status, np.int32)
+    sl = None if slot is None else _c(slot, np.int32)
     rc = lib().oracle_commit(_p(km.view(np.uint8)), _p(kb.view(np.uint8)), L, B, Hkv, cap, row_bytes, M,
                              _p(tm), _p(tt), _p(ln), _p(lm), _p(pos), _p(_c(path, np.int32)),
-                             _p(_c(accept_len, np.int32)), _p(st))
+                             _p(_c(accept_len, np.int32)), _p(st), int(mode), _p(sl), rows)
     return rc, km, tm, ln, int(lm[0]), pos
+
+
+def realign(kv_main: np.ndarray, lens, ends, tokens_main=None, slot=None, want_pos_ids: bool = True):
+    """Moves each sequence's content [end_b - len_b, end_b) to end at the
+    largest end.  kv_main [L][2][rows][Hkv][cap][...].  Works on copies;
+    returns (rc, kv_main', tokens_main', lmax', pos_ids)."""
+    km = np.array(kv_main, copy=True, order="C")
+    L, _, rows, Hkv, cap = km.shape[:5]
+    B = len(lens)
+    row_bytes = km[0, 0, 0, 0, 0].nbytes if km.size else 0
+    tm = None if tokens_main is None else np.array(tokens_main, dtype=np.int32, copy=True, order="C")
+    pos = np.zeros((rows, cap), dtype=np.int32) if want_pos_ids else None
+    sl = None if slot is None else _c(slot, np.int32)
+    lm = np.zeros(1, dtype=np.int32)
+    rc = lib().oracle_realign(_p(km.view(np.uint8)), L, B, Hkv, cap, row_bytes, _p(tm), _p(pos), _p(sl), rows,
+                              _p(_c(lens, np.int32)), _p(_c(ends, np.int32)), _p(lm))
+    return rc, km, tm, int(lm[0]), pos

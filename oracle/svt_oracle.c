@@ -258,30 +258,40 @@ void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_
 /* content and appends what it accepted (unpad, append, repad), so that      */
 /* padding + content equals the batch maximum for every sequence             */
 /* (rectangular alignment) and position ids run from 0 over the content.     */
+/* Cross-batch scheduling (EXSPEC) batches sequences of equal length, whose  */
+/* batch needs no realignment: the accepted rows are simply appended.        */
 /* [EP-ko] §2 / [EP-nl] §2.A: the accepted rows come from the branch cache   */
 /* by path index, and only the new segment is reordered.                     */
 /* Readings: the committed rows are the root plus the accepted drafts        */
 /* (A_b = accept_len_b + 1 rows: path[b][0..A_b)); sequences with a nonzero  */
 /* status append nothing but still follow the new alignment; padding sits on */
-/* the left; pos_ids padding is 0; columns >= new lmax are left untouched.   */
+/* the left; pos_ids padding is 0; columns past a sequence's new end are     */
+/* left untouched.  In append mode every sequence keeps its start column     */
+/* lmax - len_b, so the new batch maximum is lmax + max_b A_b.               */
 /* ------------------------------------------------------------------------ */
+static int slot_of(const int32_t* slot, int32_t b) { return slot ? slot[b] : b; }
+
 int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, int32_t B,
                   int32_t Hkv, int64_t cap, int32_t row_bytes, int32_t M,
                   int32_t* tokens_main, const int32_t* tree_tokens, int32_t* len, int32_t* lmax,
                   int32_t* pos_ids, const int32_t* path, const int32_t* accept_len,
-                  const int32_t* status) {
+                  const int32_t* status, int32_t mode, const int32_t* slot, int32_t rows) {
   int32_t T = M + 1;
   int32_t old_lmax = *lmax;
-  /* Inconsistent lengths are reported before bad accept results, which are
-   * reported before a capacity overflow; in every case nothing changes. */
+  if (!slot) rows = B;
+  /* Inconsistent lengths are reported before bad accept results or slots,
+   * which are reported before a capacity overflow; in every case nothing
+   * changes. */
   if (old_lmax < 0 || (int64_t)old_lmax > cap) return ORACLE_ERR_LENGTH;
   for (int32_t b = 0; b < B; ++b)
     if (len[b] < 0 || len[b] > old_lmax) return ORACLE_ERR_LENGTH;
   int32_t* A = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
-  int32_t new_lmax = 0;
+  int32_t* start = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+  int32_t new_lmax = mode == 1 ? old_lmax : 0;
   int arg_bad = 0;
   for (int32_t b = 0; b < B; ++b) {
     int valid = !(status && status[b] != 0);
+    if (slot_of(slot, b) < 0 || slot_of(slot, b) >= rows) arg_bad = 1;
     A[b] = 0;
     if (valid) {
       if (accept_len[b] < 0 || accept_len[b] > M) {
@@ -292,53 +302,103 @@ int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, 
           if (path[(int64_t)b * T + k] < 0 || path[(int64_t)b * T + k] > M) arg_bad = 1;
       }
     }
-    if (len[b] + A[b] > new_lmax) new_lmax = len[b] + A[b];
+    int32_t new_end = mode == 1 ? old_lmax + A[b] : len[b] + A[b];
+    if (new_end > new_lmax) new_lmax = new_end;
   }
-  if (arg_bad) { free(A); return ORACLE_ERR_ARG; }
-  if ((int64_t)new_lmax > cap) { free(A); return ORACLE_ERR_CAPACITY; }
+  if (arg_bad) { free(A); free(start); return ORACLE_ERR_ARG; }
+  if ((int64_t)new_lmax > cap) { free(A); free(start); return ORACLE_ERR_CAPACITY; }
+  /* New start column of each sequence's content. */
+  for (int32_t b = 0; b < B; ++b)
+    start[b] = mode == 1 ? old_lmax - len[b] : new_lmax - (len[b] + A[b]);
 
   /* Per sequence: build the logical row list (old content, then the accepted
-   * branch rows in path order), then write it back left-padded to new_lmax. */
+   * branch rows in path order), then write it back from its new start. */
   uint8_t* tmp = (uint8_t*)malloc((size_t)(new_lmax > 0 ? new_lmax : 1) * (size_t)row_bytes);
   for (int32_t l = 0; l < n_layers; ++l)
     for (int32_t kv = 0; kv < 2; ++kv)
       for (int32_t b = 0; b < B; ++b)
         for (int32_t h = 0; h < Hkv; ++h) {
-          int64_t slab = (((int64_t)l * 2 + kv) * B + b) * Hkv + h;
+          int64_t slab = (((int64_t)l * 2 + kv) * rows + slot_of(slot, b)) * Hkv + h;
+          int64_t bslab = (((int64_t)l * 2 + kv) * B + b) * Hkv + h;
           uint8_t* main_s = kv_main + slab * cap * row_bytes;
-          const uint8_t* br_s = kv_branch + slab * (int64_t)T * row_bytes;
-          int32_t old_pad = old_lmax - len[b];
+          const uint8_t* br_s = kv_branch + bslab * (int64_t)T * row_bytes;
           int32_t n = 0;
-          for (int32_t c = old_pad; c < old_lmax; ++c, ++n)
+          for (int32_t c = old_lmax - len[b]; c < old_lmax; ++c, ++n)
             memcpy(tmp + (int64_t)n * row_bytes, main_s + (int64_t)c * row_bytes, (size_t)row_bytes);
           for (int32_t k = 0; k < A[b]; ++k, ++n)
             memcpy(tmp + (int64_t)n * row_bytes, br_s + (int64_t)path[(int64_t)b * T + k] * row_bytes,
                    (size_t)row_bytes);
-          int32_t new_pad = new_lmax - n;
-          memcpy(main_s + (int64_t)new_pad * row_bytes, tmp, (size_t)n * (size_t)row_bytes);
+          memcpy(main_s + (int64_t)start[b] * row_bytes, tmp, (size_t)n * (size_t)row_bytes);
         }
   free(tmp);
 
   int32_t* ttmp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(new_lmax > 0 ? new_lmax : 1));
   for (int32_t b = 0; b < B; ++b) {
     int32_t new_len = len[b] + A[b];
-    int32_t new_pad = new_lmax - new_len;
+    int32_t row = slot_of(slot, b);
     if (tokens_main) {
-      int32_t* tm = tokens_main + (int64_t)b * cap;
+      int32_t* tm = tokens_main + (int64_t)row * cap;
       int32_t n = 0;
       for (int32_t c = old_lmax - len[b]; c < old_lmax; ++c) ttmp[n++] = tm[c];
       for (int32_t k = 0; k < A[b]; ++k)
         ttmp[n++] = tree_tokens[(int64_t)b * T + path[(int64_t)b * T + k]];
-      for (int32_t x = 0; x < n; ++x) tm[new_pad + x] = ttmp[x];
+      for (int32_t x = 0; x < n; ++x) tm[start[b] + x] = ttmp[x];
     }
     if (pos_ids) {
-      int32_t* pp = pos_ids + (int64_t)b * cap;
-      for (int32_t c = 0; c < new_lmax; ++c) pp[c] = c < new_pad ? 0 : c - new_pad;
+      int32_t* pp = pos_ids + (int64_t)row * cap;
+      for (int32_t c = 0; c < start[b] + new_len; ++c) pp[c] = c < start[b] ? 0 : c - start[b];
     }
   }
   free(ttmp);
   for (int32_t b = 0; b < B; ++b) len[b] += A[b];
   *lmax = new_lmax;
   free(A);
+  free(start);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Realignment.  [BSD] §2: when a batch mixes lengths, EXSPEC falls back to  */
+/* EQSPEC's alignment: padding + content must equal the batch maximum for    */
+/* every sequence.  Reading: the common end is the largest current end, so   */
+/* the sequence(s) already ending there stay put.                            */
+/* ------------------------------------------------------------------------ */
+int oracle_realign(uint8_t* kv_main, int32_t n_layers, int32_t B, int32_t Hkv, int64_t cap,
+                   int32_t row_bytes, int32_t* tokens_main, int32_t* pos_ids, const int32_t* slot,
+                   int32_t rows, const int32_t* len, const int32_t* end, int32_t* lmax) {
+  if (!slot) rows = B;
+  int32_t E = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (len[b] < 0 || end[b] < len[b] || (int64_t)end[b] > cap) return ORACLE_ERR_LENGTH;
+    if (end[b] > E) E = end[b];
+  }
+  for (int32_t b = 0; b < B; ++b)
+    if (slot_of(slot, b) < 0 || slot_of(slot, b) >= rows) return ORACLE_ERR_ARG;
+  uint8_t* tmp = (uint8_t*)malloc((size_t)(E > 0 ? E : 1) * (size_t)row_bytes);
+  for (int32_t l = 0; l < n_layers; ++l)
+    for (int32_t kv = 0; kv < 2; ++kv)
+      for (int32_t b = 0; b < B; ++b)
+        for (int32_t h = 0; h < Hkv; ++h) {
+          int64_t slab = (((int64_t)l * 2 + kv) * rows + slot_of(slot, b)) * Hkv + h;
+          uint8_t* main_s = kv_main + slab * cap * row_bytes;
+          memcpy(tmp, main_s + (int64_t)(end[b] - len[b]) * row_bytes, (size_t)len[b] * (size_t)row_bytes);
+          memcpy(main_s + (int64_t)(E - len[b]) * row_bytes, tmp, (size_t)len[b] * (size_t)row_bytes);
+        }
+  free(tmp);
+  int32_t* ttmp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t row = slot_of(slot, b);
+    if (tokens_main) {
+      int32_t* tm = tokens_main + (int64_t)row * cap;
+      for (int32_t x = 0; x < len[b]; ++x) ttmp[x] = tm[end[b] - len[b] + x];
+      for (int32_t x = 0; x < len[b]; ++x) tm[E - len[b] + x] = ttmp[x];
+    }
+    if (pos_ids) {
+      int32_t* pp = pos_ids + (int64_t)row * cap;
+      for (int32_t c = 0; c < E; ++c) pp[c] = c < E - len[b] ? 0 : c - (E - len[b]);
+    }
+  }
+  free(ttmp);
+  *lmax = E;
   return ORACLE_OK;
 }

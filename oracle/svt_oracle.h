@@ -82,21 +82,37 @@ void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_
                    const int32_t* status, int32_t B, int32_t M,
                    int32_t* accept_len, int32_t* path, int32_t* bonus);
 
-/* KV commit with EQSPEC re-padding ([BSD] §2 Methodology: rectangular
- * alignment, position-id contiguity, unpad-append-repad; [EP-ko] §2 fast
- * reorder by path_indices; [EP-nl] §2.A commit modes).
- *   kv_main   [L][2][B][Hkv][cap][row_bytes]  in/out (raw bytes)
+/* KV commit ([BSD] §2 Methodology: rectangular alignment, position-id
+ * contiguity, unpad-append-repad (EQSPEC); equal-length batches of
+ * cross-batch scheduling need no realignment (EXSPEC); [EP-ko] §2 fast reorder
+ * by path_indices; [EP-nl] §2.A commit modes).
+ *   kv_main   [L][2][rows][Hkv][cap][row_bytes]  in/out (raw bytes)
  *   kv_branch [L][2][B][Hkv][T][row_bytes]
- *   tokens_main [B][cap] in/out (nullable), tree_tokens [B][T]
- *   len [B], lmax [1] in/out, pos_ids [B][cap] out (nullable)
+ *   tokens_main [rows][cap] in/out (nullable), tree_tokens [B][T]
+ *   len [B], lmax [1] in/out, pos_ids [rows][cap] out (nullable)
+ *   slot [B] or NULL: sequence b is row slot[b] of kv_main, tokens_main and
+ *   pos_ids (rows = B when NULL)
+ *   mode 0 = re-pad (EQSPEC), 1 = append without moving (EXSPEC)
  * Returns 0, or on error (nothing changes) ORACLE_ERR_LENGTH for inconsistent
- * lengths, ORACLE_ERR_ARG for an accept length or path entry outside [0, M],
- * ORACLE_ERR_CAPACITY when the new lmax would exceed cap (checked in that order). */
+ * lengths, ORACLE_ERR_ARG for an accept length or path entry outside [0, M]
+ * or a slot outside [0, rows), ORACLE_ERR_CAPACITY when a sequence would end
+ * past cap (checked in that order). */
 int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, int32_t B,
                   int32_t Hkv, int64_t cap, int32_t row_bytes, int32_t M,
                   int32_t* tokens_main, const int32_t* tree_tokens, int32_t* len, int32_t* lmax,
                   int32_t* pos_ids, const int32_t* path, const int32_t* accept_len,
-                  const int32_t* status);
+                  const int32_t* status, int32_t mode, const int32_t* slot, int32_t rows);
+
+/* Realignment of a batch whose sequences end at different columns to the
+ * largest end ([BSD] §2: the EXSPEC fallback uses EQSPEC's alignment when a
+ * batch mixes lengths).  Sequence b's content [end_b - len_b, end_b) is
+ * rewritten at [E - len_b, E), E = max_b end_b, in every slab of kv_main and
+ * in tokens_main; pos_ids for c < E.  *lmax = E.  Returns 0, or (nothing
+ * changes) ORACLE_ERR_LENGTH when some len_b < 0, end_b < len_b or
+ * end_b > cap, else ORACLE_ERR_ARG for a slot outside [0, rows). */
+int oracle_realign(uint8_t* kv_main, int32_t n_layers, int32_t B, int32_t Hkv, int64_t cap,
+                   int32_t row_bytes, int32_t* tokens_main, int32_t* pos_ids, const int32_t* slot,
+                   int32_t rows, const int32_t* len, const int32_t* end, int32_t* lmax);
 
 #ifdef __cplusplus
 }
