@@ -9,6 +9,10 @@
  *   svt_accept            greedy argmax per node, longest accepted root path
  *   svt_commit            append the accepted rows to the main cache, re-pad
  *
+ * plus svt_realign (bring a batch drawn from a sequence pool to a common end
+ * column) and svt_pool_pick (host: choose the next batch from a pool) for
+ * cross-batch scheduling.
+ *
  * Sources (summary pages of two papers):
  *   [EP-ko] "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend
  *           NPUs", gist.science Korean summary.
@@ -99,7 +103,10 @@ int svt_build_mask(const int32_t* parents, int32_t B, int32_t M, uint64_t* mask,
 /*   out[b][i][h] = softmax(scale * q[b][i][h] . key) weighted sum of values  */
 /* The prefix is left padded: every sequence's content ends at column lmax    */
 /* ([BSD] section 2, rectangular alignment).  Columns outside the content are */
-/* never read.  Accumulation and softmax are fp32; bf16 inputs use bf16 MFMA  */
+/* never read.  With seq_slot set, sequence b's cache rows are                 */
+/* k_cache[seq_slot[b]] and v_cache[seq_slot[b]] of a pool of n_slots rows     */
+/* (q, tree KV, mask and out stay indexed by b); a slot outside [0, n_slots)  */
+/* gives that sequence SVT_ERR_ARG in seq_status and zero output.  Accumulation and softmax are fp32; bf16 inputs use bf16 MFMA  */
 /* for both contractions (probabilities are rounded to bf16 for the second).  */
 /* The result is bitwise deterministic run to run.                            */
 /* ------------------------------------------------------------------------ */
@@ -125,6 +132,8 @@ typedef struct svt_attn_args {
   void* workspace;           /* device scratch, svt_verify_attention_workspace bytes  */
   size_t workspace_bytes;
   int32_t form;              /* svt_attn_form: which work decomposition (bf16 only)   */
+  const int32_t* seq_slot;   /* [B] cache row of each sequence, or NULL (row b)        */
+  int32_t n_slots;           /* rows of k_cache / v_cache when seq_slot is set         */
 } svt_attn_args;
 
 /* Work decomposition of svt_verify_attention (bf16; fp32 always splits).
@@ -135,7 +144,7 @@ typedef struct svt_attn_args {
  *                    result does not depend on the rest of the batch
  *   SVT_ATTN_STREAM  the key tiles of the whole batch cut into one equal
  *                    range per compute unit (needs three or more 16-row query
- *                    tiles per KV head and B <= 2048, else SVT_ERR_UNSUPPORTED) */
+ *                    tiles per KV head and B <= 1024, else SVT_ERR_UNSUPPORTED) */
 typedef enum svt_attn_form { SVT_ATTN_AUTO = 0, SVT_ATTN_SPLIT = 1, SVT_ATTN_STREAM = 2 } svt_attn_form;
 
 /* Bytes of workspace svt_verify_attention needs for these shapes (pointer
@@ -193,6 +202,18 @@ int svt_accept(const svt_accept_args* a, hipStream_t stream);
 /*   head, and for tokens_main (with tree_tokens[b][path[b][k]]).             */
 /*   pos_ids[b][c] = c - pad'_b on content, 0 on padding, for c < lmax'.      */
 /*   Columns >= lmax' are not written; padding contents are unspecified.      */
+/* mode SVT_COMMIT_APPEND is the no-realignment path of cross-batch          */
+/* scheduling ([BSD] section 2, EXSPEC: a batch of equal-length sequences    */
+/* needs no realignment): nothing moves; rows path[b][0..A_b) go to          */
+/* [lmax, lmax + A_b) after the unchanged content [lmax - len_b, lmax);      */
+/* len' = len + A, lmax' = lmax + max_b A_b, and sequence b's content now     */
+/* ends at lmax + A_b (the batch stays rectangular only where A_b = max A).  */
+/* pos_ids[b][c] = c - (lmax - len_b) on content, 0 on padding, for           */
+/* c < lmax + A_b.  SVT_ERR_CAPACITY when lmax + A_b > cap for some b.        */
+/* With seq_slot set, sequence b lives in row seq_slot[b] of kv_main,         */
+/* tokens_main and pos_ids (pools of n_slots rows; kv_branch, tree_tokens,    */
+/* len, path, accept_len stay indexed by b).  The slots must be distinct; one */
+/* outside [0, n_slots) is SVT_ERR_ARG (checked with the accept arguments).   */
 /* Rows are moved as raw bytes (any bit pattern survives).  Device-side     */
 /* errors are checked over the whole batch in this order, the first one found */
 /* goes to commit_status and then nothing is written:                         */
@@ -217,9 +238,66 @@ typedef struct svt_commit_args {
   const int32_t* accept_len;   /* [B] from svt_accept                                */
   const int32_t* status;       /* [B] or NULL                                        */
   int32_t* commit_status;      /* [1] out: SVT_OK or one of the errors above        */
+  const int32_t* seq_slot;     /* [B] pool row of each sequence, or NULL (row b)     */
+  int32_t n_slots;             /* pool rows when seq_slot is set                     */
+  int32_t mode;                /* svt_commit_mode                                    */
 } svt_commit_args;
 
+typedef enum svt_commit_mode { SVT_COMMIT_REPAD = 0, SVT_COMMIT_APPEND = 1 } svt_commit_mode;
+
 int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* svt_realign                                                               */
+/* Brings a batch whose sequences end at different columns to a common end   */
+/* ([BSD] section 2: EXSPEC falls back to EQSPEC's alignment when a batch     */
+/* mixes lengths; rectangular alignment).  Sequence b's content               */
+/* [end[b] - len[b], end[b]) moves to [E - len[b], E) with E = max_b end[b],  */
+/* in every layer, K and V plane and KV head, and in tokens_main; nothing     */
+/* else changes.  pos_ids[b][c] = c - (E - len[b]) on content, 0 on padding,  */
+/* for c < E.  *lmax = E afterwards (0 for B = 0).  Errors, found on the      */
+/* device before anything is written (then nothing is): SVT_ERR_LENGTH when   */
+/* some len[b] < 0, end[b] < len[b] or end[b] > cap, else SVT_ERR_ARG for a   */
+/* slot outside [0, n_slots).  Rows move as raw bytes.                        */
+/* ------------------------------------------------------------------------ */
+typedef struct svt_realign_args {
+  int32_t B, Hkv, D, n_layers;
+  int32_t dtype;               /* svt_dtype (element size of cache rows)            */
+  int64_t cap;
+  void* kv_main;               /* [n_layers][2][rows][Hkv][cap][D] in/out           */
+  int32_t* tokens_main;        /* [rows][cap] in/out, or NULL                        */
+  int32_t* pos_ids;            /* [rows][cap] out, or NULL                           */
+  const int32_t* seq_slot;     /* [B] pool row of each sequence, or NULL (rows = B)  */
+  int32_t n_slots;             /* pool rows when seq_slot is set                     */
+  const int32_t* len;          /* [B] content length                                 */
+  const int32_t* end;          /* [B] column just past each sequence's content       */
+  int32_t* lmax;               /* [1] out: the common end E                          */
+  int32_t* realign_status;     /* [1] out: SVT_OK or one of the errors above         */
+} svt_realign_args;
+
+int svt_realign(const svt_realign_args* a, int32_t flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* svt_pool_pick (host)                                                       */
+/* Chooses the next batch of cross-batch scheduling ([BSD] section 2, EXSPEC: */
+/* a SequencePool; sequences whose lengths match are grouped so their batch   */
+/* needs no realignment; otherwise EQSPEC's alignment is the fallback).       */
+/* Pool sequences with active_host[s] != 0 are grouped by end column          */
+/* end_host[s] (for sequences stored without padding this is their length).   */
+/* If the largest group (ties: smallest end) holds at least                   */
+/* min(max_batch, min_group) sequences, the batch is up to max_batch of them, */
+/* lowest slots first.  Otherwise the batch is that group filled up to        */
+/* max_batch with the active sequences whose end is nearest to the group's    */
+/* (ties: smaller end, then lower slot).  slots_host receives the chosen      */
+/* slots in increasing order and *n_host their count (0 when no sequence is   */
+/* active).  Returns 1 when every chosen slot has the same end (commit with   */
+/* SVT_COMMIT_APPEND, no realignment; also for an empty pick), 0 when the     */
+/* ends differ (svt_realign first, then a SVT_COMMIT_REPAD commit), or        */
+/* SVT_ERR_ARG for n_slots < 0, max_batch < 1, min_group < 1 or a NULL        */
+/* pointer.  Pure host code; no device work.                                  */
+/* ------------------------------------------------------------------------ */
+int svt_pool_pick(const int32_t* end_host, const int32_t* active_host, int32_t n_slots, int32_t max_batch,
+                  int32_t min_group, int32_t* slots_host, int32_t* n_host);
 
 /* ------------------------------------------------------------------------ */
 /* Utilities                                                                  */

@@ -65,8 +65,11 @@ _C_TO_CTYPES = {
 }
 
 
-@pytest.mark.parametrize("cname,pyname", [("svt_attn_args", "AttnArgs"), ("svt_accept_args", "AcceptArgs"),
-                                          ("svt_commit_args", "CommitArgs")])
+STRUCTS = [("svt_attn_args", "AttnArgs"), ("svt_accept_args", "AcceptArgs"), ("svt_commit_args", "CommitArgs"),
+           ("svt_realign_args", "RealignArgs")]
+
+
+@pytest.mark.parametrize("cname,pyname", STRUCTS)
 def test_binding_structs_match_header(cname, pyname):
     fields = _structs(_header())[cname]
     py = getattr(svt, pyname)._fields_
@@ -84,7 +87,7 @@ def test_struct_sizes_match_the_c_compiler(tmp_path):
     text = _header()
     structs = _structs(text)
     src = ["#include <stdio.h>", "#include <stddef.h>", '#include "svt.h"', "int main(void) {"]
-    for cname in ["svt_attn_args", "svt_accept_args", "svt_commit_args"]:
+    for cname, _ in STRUCTS:
         src.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
         for _, f in structs[cname]:
             src.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
@@ -100,8 +103,7 @@ def test_struct_sizes_match_the_c_compiler(tmp_path):
         pytest.skip(f"host compile of svt.h unavailable: {e}")
     got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True, text=True,
                                                               check=True).stdout.split("\n") if line)
-    for cname, pyname in [("svt_attn_args", "AttnArgs"), ("svt_accept_args", "AcceptArgs"),
-                          ("svt_commit_args", "CommitArgs")]:
+    for cname, pyname in STRUCTS:
         py = getattr(svt, pyname)
         assert int(got[cname]) == ctypes.sizeof(py), cname
         for _, f in structs[cname]:

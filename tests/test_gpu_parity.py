@@ -358,7 +358,7 @@ FORM_IDS = ["auto", "split", "stream"]
 
 
 def _stream_ok(w):
-    return w.dtype == "bf16" and (w.G * w.T + 15) // 16 >= 3 and w.B <= 2048
+    return w.dtype == "bf16" and (w.G * w.T + 15) // 16 >= 3 and w.B <= 1024
 
 
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)

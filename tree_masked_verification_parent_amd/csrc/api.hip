@@ -59,10 +59,11 @@ int svt_verify_attention(const svt_attn_args* a, hipStream_t stream) {
       a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap || !(a->scale >= 0.0f))
     return finish("svt_verify_attention", SVT_ERR_ARG, shape);
   if (a->form < SVT_ATTN_AUTO || a->form > SVT_ATTN_STREAM) return finish("svt_verify_attention", SVT_ERR_ARG, shape);
+  if (a->seq_slot && a->n_slots <= 0) return finish("svt_verify_attention", SVT_ERR_ARG, shape);
   if (a->M >= SVT_MAX_T || (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
     return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);
   if (a->form == SVT_ATTN_STREAM &&
-      (a->dtype != SVT_BF16 || ((a->Hq / a->Hkv) * (a->M + 1) + 15) / 16 < 3 || a->B > 2048))
+      (a->dtype != SVT_BF16 || ((a->Hq / a->Hkv) * (a->M + 1) + 15) / 16 < 3 || a->B > svt::kStreamMaxBatch))
     return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);
   if (a->B == 0) return finish("svt_verify_attention", SVT_OK, shape);
   if (!a->q || !a->k_cache || !a->v_cache || !a->len || !a->lmax || !a->k_tree || !a->v_tree || !a->mask ||
@@ -105,10 +106,12 @@ int svt_accept(const svt_accept_args* a, hipStream_t stream) {
 int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream) {
   char shape[128];
   if (!a) return finish("svt_commit", SVT_ERR_ARG, "null args");
-  std::snprintf(shape, sizeof shape, "B=%d M=%d Hkv=%d D=%d layers=%d dtype=%d cap=%lld", a->B, a->M, a->Hkv, a->D,
-                a->n_layers, a->dtype, (long long)a->cap);
+  std::snprintf(shape, sizeof shape, "B=%d M=%d Hkv=%d D=%d layers=%d dtype=%d cap=%lld mode=%d slots=%d", a->B, a->M,
+                a->Hkv, a->D, a->n_layers, a->dtype, (long long)a->cap, a->mode, a->seq_slot ? a->n_slots : -1);
   if (a->B < 0 || a->M < 0 || a->Hkv < 0 || a->D <= 0 || a->n_layers < 0 || a->cap < 0 || a->cap > 0x7FFFFFFF)
     return finish("svt_commit", SVT_ERR_ARG, shape);
+  if (a->mode != SVT_COMMIT_REPAD && a->mode != SVT_COMMIT_APPEND) return finish("svt_commit", SVT_ERR_ARG, shape);
+  if (a->seq_slot && a->n_slots <= 0) return finish("svt_commit", SVT_ERR_ARG, shape);
   if (a->M >= SVT_MAX_T || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
     return finish("svt_commit", SVT_ERR_UNSUPPORTED, shape);
   const int esize = a->dtype == SVT_FP32 ? 4 : 2;
@@ -122,6 +125,33 @@ int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream) {
   int rc = hip_rc(svt::launch_commit(a, stream));
   if (rc == SVT_OK && (flags & SVT_SYNC_CHECK)) rc = svt_check_status(a->commit_status, 1, stream);
   return finish("svt_commit", rc, shape);
+}
+
+int svt_realign(const svt_realign_args* a, int32_t flags, hipStream_t stream) {
+  char shape[128];
+  if (!a) return finish("svt_realign", SVT_ERR_ARG, "null args");
+  std::snprintf(shape, sizeof shape, "B=%d Hkv=%d D=%d layers=%d dtype=%d cap=%lld slots=%d", a->B, a->Hkv, a->D,
+                a->n_layers, a->dtype, (long long)a->cap, a->seq_slot ? a->n_slots : -1);
+  if (a->B < 0 || a->Hkv < 0 || a->D <= 0 || a->n_layers < 0 || a->cap < 0 || a->cap > 0x7FFFFFFF)
+    return finish("svt_realign", SVT_ERR_ARG, shape);
+  if (a->dtype != SVT_FP32 && a->dtype != SVT_BF16) return finish("svt_realign", SVT_ERR_UNSUPPORTED, shape);
+  const int esize = a->dtype == SVT_FP32 ? 4 : 2;
+  if ((a->D * esize) % 16 != 0) return finish("svt_realign", SVT_ERR_UNSUPPORTED, shape);
+  if (!a->len || !a->end || !a->lmax || !a->realign_status || (a->seq_slot && a->n_slots <= 0))
+    return finish("svt_realign", SVT_ERR_ARG, shape);
+  const bool has_kv = a->n_layers > 0 && a->Hkv > 0 && a->B > 0;
+  if (has_kv && (!a->kv_main || !aligned(a->kv_main, 16))) return finish("svt_realign", SVT_ERR_ARG, shape);
+  int rc = hip_rc(svt::launch_realign(a, stream));
+  if (rc == SVT_OK && (flags & SVT_SYNC_CHECK)) rc = svt_check_status(a->realign_status, 1, stream);
+  return finish("svt_realign", rc, shape);
+}
+
+int svt_pool_pick(const int32_t* end_host, const int32_t* active_host, int32_t n_slots, int32_t max_batch,
+                  int32_t min_group, int32_t* slots_host, int32_t* n_host) {
+  if (n_slots < 0 || max_batch < 1 || min_group < 1 || !n_host || (n_slots > 0 && (!end_host || !active_host)) ||
+      !slots_host)
+    return SVT_ERR_ARG;
+  return svt::pool_pick(end_host, active_host, n_slots, max_batch, min_group, slots_host, n_host);
 }
 
 int svt_check_status(const int32_t* status, int32_t n, hipStream_t stream) {

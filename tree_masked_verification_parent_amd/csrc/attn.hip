@@ -62,6 +62,7 @@ struct AttnDev {
   const int32_t* len;
   const int32_t* lmax;
   const int32_t* status;
+  const int32_t* slot;  // sequence -> cache row of k/v_cache, or NULL (identity)
   void* out;
   int32_t* seq_status;
   float* ws_o;   // split partials [B][Hkv][ns][R][D]; stream partials [2*grid][qb_rows][D]
@@ -70,13 +71,25 @@ struct AttnDev {
   int64_t cap;
   int B, T, Hq, Hkv, G, R, W;
   int lmax_bound, kc, ns, nqb, qb_rows, nunits;
+  int n_slots;      // cache rows when slot is set
   int stream_grid;  // workgroups of the stream form
   float scale_log2;
 };
 
+// Why sequence b is skipped (SVT_OK: it is not): its tree status, a cache
+// row outside the pool, or lengths outside 0 <= len <= lmax <= lmax_bound.
+__device__ __forceinline__ int seq_code(const AttnDev& a, int b, int lmax, int L) {
+  const int st = a.status ? a.status[b] : SVT_OK;
+  const int row = a.slot ? a.slot[b] : b;
+  if (st != SVT_OK) return st;
+  if (row < 0 || row >= a.n_slots) return SVT_ERR_ARG;
+  return (lmax >= 0 && lmax <= a.lmax_bound && L >= 0 && L <= lmax) ? SVT_OK : SVT_ERR_LENGTH;
+}
+
 // Decoded workgroup coordinates and the sequence's key ranges.
 struct WgCtx {
   int b, g, split, qb;
+  int64_t cg;      // cache slab (cache row * Hkv + g)
   int code;        // SVT_OK or why the sequence is skipped
   int L, lmax;
   int ns_b;        // splits this sequence uses
@@ -101,9 +114,8 @@ __device__ __forceinline__ bool decode_wg(const AttnDev& a, WgCtx& c) {
   c.split = unit / (a.Hkv * a.B);
   c.lmax = *a.lmax;
   c.L = a.len[c.b];
-  const int st = a.status ? a.status[c.b] : SVT_OK;
-  const bool len_ok = c.lmax >= 0 && c.lmax <= a.lmax_bound && c.L >= 0 && c.L <= c.lmax;
-  c.code = st != SVT_OK ? st : (len_ok ? SVT_OK : SVT_ERR_LENGTH);
+  c.code = seq_code(a, c.b, c.lmax, c.L);
+  c.cg = (int64_t)(c.code == SVT_OK ? (a.slot ? a.slot[c.b] : c.b) : 0) * a.Hkv + c.g;
   c.ns_b = c.code == SVT_OK ? max(1, (c.L + a.kc - 1) / a.kc) : 1;
   if (c.split >= c.ns_b) return false;
   c.k_beg = c.split * a.kc;
@@ -337,8 +349,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
     if (t < c.n_ptiles) {
       const int k0 = c.k_beg + t * KT;
       const int64_t col = (int64_t)pad + k0;
-      kb = kc + (bg * a.cap + col) * D;
-      vb = vc + (bg * a.cap + col) * D;
+      kb = kc + (c.cg * a.cap + col) * D;
+      vb = vc + (c.cg * a.cap + col) * D;
       nvalid = min(KT, c.k_end - k0);
     } else {
       const int j0 = (t - c.n_ptiles) * KT;
@@ -593,15 +605,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 // attn_stream_combine_kernel merges them in stream order.  No workgroup waits
 // for another, and the result does not depend on timing.
 // --------------------------------------------------------------------------
-constexpr int kStreamMaxB = 2048;
+constexpr int kStreamMaxB = kStreamMaxBatch;
 
 // Key tiles one unit of sequence b holds (prefix tiles + tree tiles), or 0
 // when the sequence is skipped; *code says why.
 __device__ __forceinline__ int stream_seq_tiles(const AttnDev& a, int b, int lmax, int* code) {
-  const int st = a.status ? a.status[b] : SVT_OK;
   const int L = a.len[b];
-  const bool len_ok = lmax >= 0 && lmax <= a.lmax_bound && L >= 0 && L <= lmax;
-  *code = st != SVT_OK ? st : (len_ok ? SVT_OK : SVT_ERR_LENGTH);
+  *code = seq_code(a, b, lmax, L);
   return *code == SVT_OK ? (L + KT - 1) / KT + (a.T + KT - 1) / KT : 0;
 }
 
@@ -620,6 +630,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * TL::STAGEB];
   __shared__ int s_pref[kStreamMaxB + 1];  // s_pref[b] = tiles of sequences < b (per unit)
   __shared__ int s_len[kStreamMaxB];
+  __shared__ int s_row[kStreamMaxB];  // cache row of each sequence
   __shared__ int s_wsum[NW];
   __shared__ int s_carry;
   __shared__ uint64_t s_mask[NW * QMAX * 16][4];  // each lane's tree-mask words, its own rows only
@@ -644,6 +655,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     if (b < B) {
       v = stream_seq_tiles(a, b, lmax, &code);
       s_len[b] = a.len[b];
+      s_row[b] = a.slot ? a.slot[b] : b;
     }
     int x = v;
 #pragma unroll
@@ -691,8 +703,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     r.L = __builtin_amdgcn_readfirstlane(s_len[r.b]);
     r.np = (r.L + KT - 1) / KT;
     const int64_t bg = (int64_t)r.b * a.Hkv + r.j / a.nqb;
-    r.kp = kc + (bg * a.cap + (lmax - r.L)) * D;
-    r.vp = vc + (bg * a.cap + (lmax - r.L)) * D;
+    const int64_t cg = (int64_t)__builtin_amdgcn_readfirstlane(s_row[r.b]) * a.Hkv + r.j / a.nqb;
+    r.kp = kc + (cg * a.cap + (lmax - r.L)) * D;
+    r.vp = vc + (cg * a.cap + (lmax - r.L)) * D;
     r.kt = ktr + bg * a.T * D;
     r.vt = vtr + bg * a.T * D;
   };
@@ -1134,8 +1147,8 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
     const bool tree_tile = t >= c.n_ptiles;
     if (!tree_tile) {
       const int k0 = c.k_beg + t * KT;
-      kb = kc + (bg * a.cap + pad + k0) * D;
-      vb = vc + (bg * a.cap + pad + k0) * D;
+      kb = kc + (c.cg * a.cap + pad + k0) * D;
+      vb = vc + (c.cg * a.cap + pad + k0) * D;
       nvalid = min(KT, c.k_end - k0);
     } else {
       const int j0 = (t - c.n_ptiles) * KT;
@@ -1217,8 +1230,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
   if (r >= a.R) return;
   const int lmax = *a.lmax;
   const int L = a.len[b];
-  const int st = a.status ? a.status[b] : SVT_OK;
-  if (st != SVT_OK || !(lmax >= 0 && lmax <= a.lmax_bound && L >= 0 && L <= lmax)) return;
+  if (seq_code(a, b, lmax, L) != SVT_OK) return;
   const int ns_b = max(1, (L + a.kc - 1) / a.kc);
   if (ns_b <= 1) return;
   const int64_t base = ((int64_t)b * a.Hkv + g) * a.ns;
@@ -1347,6 +1359,8 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.len = a->len;
   d.lmax = a->lmax;
   d.status = a->status;
+  d.slot = a->seq_slot;
+  d.n_slots = a->seq_slot ? a->n_slots : a->B;
   d.out = a->out;
   d.seq_status = a->seq_status;
   if (p.wide) {

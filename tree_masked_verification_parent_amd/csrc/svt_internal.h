@@ -12,6 +12,7 @@
 namespace svt {
 
 constexpr int kWave = 64;
+constexpr int kStreamMaxBatch = 1024;  // largest batch of the stream attention form
 
 // ---- launch plans (host side), shared by the workspace query and the launch ----
 struct AttnPlan {
@@ -43,6 +44,11 @@ hipError_t launch_build_mask(const int32_t* parents, int B, int M, uint64_t* mas
 hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_accept(const svt_accept_args* a, const AcceptPlan& p, hipStream_t s);
 hipError_t launch_commit(const svt_commit_args* a, hipStream_t s);
+hipError_t launch_realign(const svt_realign_args* a, hipStream_t s);
+
+// ---- host-only scheduling (pool.cpp) ----
+int pool_pick(const int32_t* end, const int32_t* active, int n_slots, int max_batch, int min_group,
+              int32_t* slots, int32_t* n_out);
 
 // ---- small device helpers ----
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

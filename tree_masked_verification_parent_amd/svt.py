@@ -31,6 +31,7 @@ SVT_FP32 = 0
 SVT_BF16 = 1
 SVT_SYNC_CHECK = 1
 SVT_ATTN_AUTO, SVT_ATTN_SPLIT, SVT_ATTN_STREAM = 0, 1, 2
+SVT_COMMIT_REPAD, SVT_COMMIT_APPEND = 0, 1
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -42,7 +43,7 @@ class AttnArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("q", _P), ("k_cache", _P), ("v_cache", _P), ("cap", _I64),
                 ("len", _P), ("lmax", _P), ("lmax_bound", _I32), ("k_tree", _P), ("v_tree", _P), ("mask", _P),
                 ("status", _P), ("out", _P), ("seq_status", _P), ("workspace", _P),
-                ("workspace_bytes", ctypes.c_size_t), ("form", _I32)]
+                ("workspace_bytes", ctypes.c_size_t), ("form", _I32), ("seq_slot", _P), ("n_slots", _I32)]
 
 
 class AcceptArgs(ctypes.Structure):
@@ -55,11 +56,18 @@ class CommitArgs(ctypes.Structure):
     _fields_ = [("B", _I32), ("M", _I32), ("Hkv", _I32), ("D", _I32), ("n_layers", _I32), ("dtype", _I32),
                 ("cap", _I64), ("kv_main", _P), ("kv_branch", _P), ("tokens_main", _P), ("tree_tokens", _P),
                 ("len", _P), ("lmax", _P), ("pos_ids", _P), ("path", _P), ("accept_len", _P), ("status", _P),
-                ("commit_status", _P)]
+                ("commit_status", _P), ("seq_slot", _P), ("n_slots", _I32), ("mode", _I32)]
+
+
+class RealignArgs(ctypes.Structure):
+    _fields_ = [("B", _I32), ("Hkv", _I32), ("D", _I32), ("n_layers", _I32), ("dtype", _I32), ("cap", _I64),
+                ("kv_main", _P), ("tokens_main", _P), ("pos_ids", _P), ("seq_slot", _P), ("n_slots", _I32),
+                ("len", _P), ("end", _P), ("lmax", _P), ("realign_status", _P)]
 
 
 EXPORTS = ["svt_build_mask", "svt_verify_attention_workspace", "svt_verify_attention", "svt_accept_workspace",
-           "svt_accept", "svt_commit", "svt_check_status", "svt_status_string", "svt_version"]
+           "svt_accept", "svt_commit", "svt_realign", "svt_pool_pick", "svt_check_status", "svt_status_string",
+           "svt_version"]
 
 _lib = None
 
@@ -84,6 +92,10 @@ def lib():
         L.svt_accept.restype = ctypes.c_int
         L.svt_commit.argtypes = [ctypes.POINTER(CommitArgs), _I32, _P]
         L.svt_commit.restype = ctypes.c_int
+        L.svt_realign.argtypes = [ctypes.POINTER(RealignArgs), _I32, _P]
+        L.svt_realign.restype = ctypes.c_int
+        L.svt_pool_pick.argtypes = [_P, _P, _I32, _I32, _I32, _P, _P]
+        L.svt_pool_pick.restype = ctypes.c_int
         L.svt_check_status.argtypes = [_P, _I32, _P]
         L.svt_check_status.restype = ctypes.c_int
         L.svt_status_string.argtypes = [ctypes.c_int]
@@ -104,6 +116,13 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("libsvt buffers must be contiguous")
     return t.data_ptr()
+
+
+def _keep(args, *tensors):
+    """The argument structs hold raw device pointers; keep the tensors they
+    point into alive for as long as the struct is."""
+    args._tensors = tuple(t for t in tensors if t is not None)
+    return args
 
 
 def _stream(stream=None):
@@ -133,7 +152,7 @@ def _dtype_code(t):
 
 
 def attn_args(q, k_cache, v_cache, lens, lmax, lmax_bound: int, k_tree, v_tree, mask, out, status=None,
-              seq_status=None, scale: float = 0.0, workspace=None, form: int = 0) -> AttnArgs:
+              seq_status=None, scale: float = 0.0, workspace=None, form: int = 0, seq_slot=None) -> AttnArgs:
     B, T, Hq, D = q.shape
     a = AttnArgs()
     a.B, a.M, a.Hq, a.Hkv, a.D = B, T - 1, Hq, k_cache.shape[1], D
@@ -147,7 +166,9 @@ def attn_args(q, k_cache, v_cache, lens, lmax, lmax_bound: int, k_tree, v_tree, 
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.form = int(form)
-    return a
+    a.seq_slot = _ptr(seq_slot)
+    a.n_slots = k_cache.shape[0] if seq_slot is not None else 0
+    return _keep(a, q, k_cache, v_cache, lens, lmax, k_tree, v_tree, mask, out, status, seq_status, workspace, seq_slot)
 
 
 def svt_verify_attention_workspace(args: AttnArgs) -> int:
@@ -168,7 +189,7 @@ def accept_args(logits, tree_tokens, parents, mask, depth, amax, accept_len, pat
     a.amax, a.accept_len, a.path, a.bonus = _ptr(amax), _ptr(accept_len), _ptr(path), _ptr(bonus)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return a
+    return _keep(a, logits, tree_tokens, parents, mask, depth, status, amax, accept_len, path, bonus, workspace)
 
 
 def svt_accept_workspace(args: AcceptArgs) -> int:
@@ -180,8 +201,11 @@ def svt_accept(args: AcceptArgs, stream=None) -> int:
 
 
 def commit_args(kv_main, kv_branch, lens, lmax, path, accept_len, commit_status, tokens_main=None,
-                tree_tokens=None, pos_ids=None, status=None) -> CommitArgs:
-    Lyr, two, B, Hkv, cap, D = kv_main.shape
+                tree_tokens=None, pos_ids=None, status=None, seq_slot=None, mode: int = SVT_COMMIT_REPAD) -> CommitArgs:
+    Lyr, two, rows, Hkv, cap, D = kv_main.shape
+    B = kv_branch.shape[2]
+    if seq_slot is None and rows != B:
+        raise ValueError("kv_main and kv_branch disagree on the batch size (pass seq_slot for a pool)")
     a = CommitArgs()
     a.B, a.M, a.Hkv, a.D, a.n_layers = B, kv_branch.shape[4] - 1, Hkv, D, Lyr
     a.dtype = _dtype_code(kv_main)
@@ -190,7 +214,11 @@ def commit_args(kv_main, kv_branch, lens, lmax, path, accept_len, commit_status,
     a.tokens_main, a.tree_tokens = _ptr(tokens_main), _ptr(tree_tokens)
     a.len, a.lmax, a.pos_ids = _ptr(lens), _ptr(lmax), _ptr(pos_ids)
     a.path, a.accept_len, a.status, a.commit_status = _ptr(path), _ptr(accept_len), _ptr(status), _ptr(commit_status)
-    return a
+    a.seq_slot = _ptr(seq_slot)
+    a.n_slots = rows if seq_slot is not None else 0
+    a.mode = int(mode)
+    return _keep(a, kv_main, kv_branch, tokens_main, tree_tokens, lens, lmax, pos_ids, path, accept_len, status,
+                 commit_status, seq_slot)
 
 
 def svt_commit(args: CommitArgs, flags: int = 0, stream=None) -> int:
@@ -199,3 +227,39 @@ def svt_commit(args: CommitArgs, flags: int = 0, stream=None) -> int:
 
 def svt_check_status(status, n: int, stream=None) -> int:
     return lib().svt_check_status(_ptr(status), n, _stream(stream))
+
+
+def realign_args(kv_main, lens, end, lmax, realign_status, tokens_main=None, pos_ids=None,
+                 seq_slot=None) -> RealignArgs:
+    Lyr, two, rows, Hkv, cap, D = kv_main.shape
+    B = lens.shape[0]
+    if seq_slot is None and rows != B:
+        raise ValueError("kv_main rows differ from the batch size (pass seq_slot for a pool)")
+    a = RealignArgs()
+    a.B, a.Hkv, a.D, a.n_layers = B, Hkv, D, Lyr
+    a.dtype = _dtype_code(kv_main)
+    a.cap = cap
+    a.kv_main, a.tokens_main, a.pos_ids = _ptr(kv_main), _ptr(tokens_main), _ptr(pos_ids)
+    a.seq_slot = _ptr(seq_slot)
+    a.n_slots = rows if seq_slot is not None else 0
+    a.len, a.end, a.lmax, a.realign_status = _ptr(lens), _ptr(end), _ptr(lmax), _ptr(realign_status)
+    return _keep(a, kv_main, tokens_main, pos_ids, seq_slot, lens, end, lmax, realign_status)
+
+
+def svt_realign(args: RealignArgs, flags: int = 0, stream=None) -> int:
+    return lib().svt_realign(ctypes.byref(args), flags, _stream(stream))
+
+
+def svt_pool_pick(end_host, active_host, max_batch: int, min_group: int):
+    """Host call.  end_host / active_host: int32 numpy arrays of the pool.
+    Returns (rc, slots): rc 1 = equal ends, 0 = mixed, < 0 = error."""
+    import numpy as np
+    end = np.ascontiguousarray(end_host, dtype=np.int32)
+    act = np.ascontiguousarray(active_host, dtype=np.int32)
+    if end.shape != act.shape:
+        raise ValueError("end and active differ in length")
+    out = np.zeros(max(1, max_batch), dtype=np.int32)
+    n = np.zeros(1, dtype=np.int32)
+    rc = lib().svt_pool_pick(end.ctypes.data, act.ctypes.data, end.shape[0], int(max_batch), int(min_group),
+                             out.ctypes.data, n.ctypes.data)
+    return rc, out[: int(n[0])].copy()
