@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--workload", default="4", help="workload index or name (default: the B=32 ragged round)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--sched", action="store_true",
+                    help="measure the realignment overhead of EQSPEC (fixed batch, re-pad every round) against "
+                         "EXSPEC (sequence pool, equal-length batches append) instead of the round benchmark")
+    ap.add_argument("--sched-rounds", type=int, default=24)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -184,12 +188,119 @@ def cpu_baseline(w, parents, lens, logits, tokens, seed, budget_s):
     }
 
 
+def sched_bench(args):
+    """EQSPEC against EXSPEC on the B=32 workload's shapes (36 layers, GQA 32/8,
+    D=128, M=32): per round, realignment (svt_realign, EXSPEC fallback only),
+    verification (mask, attention over every layer, accept) and commit (re-pad
+    for EQSPEC and the fallback, append for equal-length EXSPEC batches), each
+    timed with HIP events.  Prints one JSON line."""
+    import torch
+    from synth import workloads as wl
+    from tree_masked_verification_parent_amd import svt
+    from tree_masked_verification_parent_amd.sched import PoolRound, SequencePool
+
+    w = wl.workload(4)
+    L, R = w.layers, args.sched_rounds
+    buckets = [1024, 1536, 2048]              # prompt lengths: few distinct values (bucketed prompts)
+    dev = torch.device("cuda")
+    gen_t = torch.Generator(device=dev)
+    gen_t.manual_seed(w.seed)
+    n_sets = 3
+    sets = []
+    for k in range(n_sets):                   # seeded trees / drafts / logits for up to 32 sequences
+        par = wl.trees(w, w.seed + 100 + k)
+        logits, tokens, _ = wl.logits_and_drafts(w, par, w.seed + 100 + k)
+        sets.append((torch.from_numpy(par).to(dev), torch.from_numpy(tokens).to(dev),
+                     torch.from_numpy(logits).to(dev)))
+    results = []
+    for B in (8, 16, 32):
+        for mode in ("eqspec", "exspec"):
+            P = B if mode == "eqspec" else 8 * B
+            cap = max(buckets) + (R + 4) * w.T + 64
+            pool = SequencePool(P, w.Hkv, w.D, L, cap, torch.bfloat16)
+            for layer in range(L):
+                pool.kv[layer].normal_(0.0, w.qkv_sigma, generator=gen_t)
+            lens = np.array([buckets[s % len(buckets)] for s in range(P)], np.int32)
+            for s in range(P):
+                pool.place(s, int(lens[s]), max(buckets) if mode == "eqspec" else None)
+            pr = PoolRound(pool, B, w.M, w.Hq, w.V, L)
+            pr.q.normal_(0.0, w.qkv_sigma, generator=gen_t)
+            pr._kvb.normal_(0.0, w.qkv_sigma, generator=gen_t)
+            stream = torch.cuda.current_stream()
+            rows = []
+            for rnd in range(R + 2):
+                if mode == "eqspec":
+                    same, slots = True, np.arange(B, dtype=np.int32)
+                else:
+                    same, slots = pool.pick(B, max(1, B // 2))
+                n = len(slots)
+                par, tok, lg = sets[rnd % n_sets]
+                pr.parents[:n].copy_(par[:n])
+                pr.tree_tokens[:n].copy_(tok[:n])
+                pr.logits[:n].copy_(lg[:n])
+                pr.load_batch(slots)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                ev[0].record(stream)
+                realigned = mode == "exspec" and not same
+                E = pool.realign(slots, pr.slot[:n], pr.len[:n], pr.end[:n]) if realigned else int(pool.end[slots[0]])
+                ev[1].record(stream)
+                rc_v = pr.verify(n, E)
+                ev[2].record(stream)
+                cmode = svt.SVT_COMMIT_APPEND if (mode == "exspec" and same) else svt.SVT_COMMIT_REPAD
+                rc_c = pr.commit(n, cmode)
+                ev[3].record(stream)
+                torch.cuda.synchronize()
+                assert rc_v == 0 and rc_c == 0 and pr.commit_status.item() == 0, \
+                    (mode, B, rnd, n, rc_v, rc_c, pr.commit_status.item())
+                al = pr.accept_len[:n].cpu().numpy()
+                pool.committed(slots, al, E, cmode)
+                if rnd >= 2:
+                    rows.append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3]),
+                                 int(n), int((al + 1).sum()), bool(realigned), cmode))
+            t_realign = sum(r[0] for r in rows) * 1e-3
+            t_verify = sum(r[1] for r in rows) * 1e-3
+            t_commit = sum(r[2] for r in rows) * 1e-3
+            t_total = t_realign + t_verify + t_commit
+            t_move = t_realign + sum(r[2] for r in rows if r[6] == svt.SVT_COMMIT_REPAD) * 1e-3
+            t_append = sum(r[2] for r in rows if r[6] == svt.SVT_COMMIT_APPEND) * 1e-3
+            toks = sum(r[4] for r in rows)
+            results.append({
+                "B": B, "mode": mode, "pool": P, "rounds": len(rows),
+                "mean_batch": float(np.mean([r[3] for r in rows])),
+                "append_rounds": sum(1 for r in rows if r[6] == svt.SVT_COMMIT_APPEND),
+                "realign_rounds": sum(1 for r in rows if r[5]),
+                "ms_realign": t_realign * 1e3, "ms_verify": t_verify * 1e3, "ms_commit": t_commit * 1e3,
+                "ms_commit_append": t_append * 1e3,
+                "realign_frac": t_move / t_total,
+                "tokens_per_s": toks / t_total,
+                "accepted_tokens": toks,
+            })
+            print(f"[sched] B={B} {mode}: realign {t_realign*1e3:.1f} ms, verify {t_verify*1e3:.1f} ms, "
+                  f"commit {t_commit*1e3:.1f} ms, realignment {t_move / t_total:.1%}, "
+                  f"{toks / t_total:.0f} tokens/s", file=sys.stderr, flush=True)
+            del pool, pr
+            torch.cuda.empty_cache()
+    out = {
+        "metric": "realignment overhead fraction of the verification round, EQSPEC vs EXSPEC",
+        "unit": "fraction of round time", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+        "data": "synthetic (seeded trees, drafts, logits; device-seeded normal caches; prompt lengths "
+                f"from {buckets})",
+        "config": {"workload": w.name + " shapes, pool scheduling", "layers": L, "rounds": R,
+                   "pool_factor_exspec": 8, "min_group": "B/2"},
+        "results": results,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(collectives and sharding are out of its scope); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sched:
+        sched_bench(args)
+        return
 
     import torch
     from synth import workloads as wl

@@ -184,6 +184,9 @@ typedef struct svt_accept_args {
   size_t workspace_bytes;
 } svt_accept_args;
 
+/* Bytes of workspace svt_accept needs for these shapes.  A smaller batch may
+ * need more (its rows are cut into more chunks to fill the chip): query it
+ * for the batch size being run, or for the largest need over the sizes used. */
 size_t svt_accept_workspace(const svt_accept_args* a);
 int svt_accept(const svt_accept_args* a, hipStream_t stream);
 

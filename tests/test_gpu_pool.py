@@ -232,3 +232,72 @@ def test_attention_seq_slot(form):
     assert not got[0].any()
     for b in (1, 2):
         assert np.abs(got[b] - good[b]).max() <= 1e-2 * max(1.0, np.abs(good[b]).max()) + 1e-3
+
+
+def test_exspec_rounds_match_oracle():
+    """Several scheduling rounds through SequencePool / PoolRound (equal-length
+    batches appended, mixed batches realigned and re-padded) leave the pool
+    exactly as the oracle replaying the same decisions."""
+    from tree_masked_verification_parent_amd.sched import PoolRound, SequencePool
+    P, B, L, Hkv, D, M, V, cap = 10, 4, 2, 2, 64, 8, 64, 160
+    T = M + 1
+    pool = SequencePool(P, Hkv, D, L, cap, torch.bfloat16)
+    km, tm = _pool(P, Hkv, L, D, cap, 2, 21)
+    pool.kv.copy_(_dev_rows(km, D, 2))
+    pool.tokens.copy_(_i32(tm))
+    lens0 = [20, 20, 20, 33, 33, 7, 20, 33, 12, 12]
+    for s, n in enumerate(lens0):
+        pool.place(s, n)
+    pr = PoolRound(pool, B, M, 4, V, attn_layers=1)
+    opos = np.zeros((P, cap), np.int32)
+    kinds = []
+    for rnd in range(8):
+        same, slots = pool.pick(B, 3)
+        n = len(slots)
+        seed = 9300 + rnd
+        trees = np.stack([gen.tree_depth_capped(gen.stream_key(seed, 5, b), M, 5) for b in range(n)]).astype(np.int32)
+        logits, des = gen.logits_with_designated_top(gen.stream_key(seed, 6), n * T, V)
+        des = des.reshape(n, T)
+        tok = np.stack([gen.plant_drafts(gen.stream_key(seed, 7, b), trees[b], des[b], V, 0.8)
+                        for b in range(n)]).astype(np.int32)
+        el = D
+        bsl = np.arange(L * 2 * n * Hkv).reshape(L, 2, n, Hkv, 1, 1) + 70000 + 100 * rnd
+        kb = gen.commit_pattern_bits(bsl, np.arange(T).reshape(1, 1, 1, 1, T, 1), np.arange(el).reshape(1, 1, 1, 1, 1, el))
+        pr.parents[:n].copy_(_i32(trees))
+        pr.tree_tokens[:n].copy_(_i32(tok))
+        pr.logits[:n].copy_(torch.from_numpy(logits.reshape(n, T, V)).to(DEV))
+        pr.kv_branch(n).copy_(_dev_rows(kb, D, 2))
+        pr.load_batch(slots)
+        lens_b, ends_b = pool.len[slots].copy(), pool.end[slots].copy()
+        print(f"round {rnd}: slots {slots.tolist()} equal_ends={same} lens {lens_b.tolist()} ends {ends_b.tolist()}",
+              flush=True)
+        if not same:
+            E = pool.realign(slots, pr.slot[:n], pr.len[:n], pr.end[:n])
+            orc, km, tm, oE, pos = oracle.realign(km, lens_b, ends_b, tokens_main=tm, slot=slots)
+            assert orc == 0 and oE == E
+            opos[slots] = pos[slots]
+        else:
+            E = int(ends_b[0])
+        assert pr.verify(n, E) == 0
+        mode = svt.SVT_COMMIT_APPEND if same else svt.SVT_COMMIT_REPAD
+        assert pr.commit(n, mode) == 0
+        torch.cuda.synchronize()
+        assert pr.commit_status.item() == 0
+        al = H.from_dev(pr.accept_len[:n])
+        oal, opath, _ = oracle.accept(oracle.argmax(logits.reshape(n, T, V)), tok, trees, M)
+        assert np.array_equal(al, oal) and np.array_equal(H.from_dev(pr.path[:n]), opath)
+        orc, km, tm, oln, olm, pos = oracle.commit(km, kb, M, tm, tok, lens_b, E, opath, oal, mode=mode, slot=slots)
+        assert orc == 0
+        opos[slots] = pos[slots]
+        pool.committed(slots, al, E, mode)
+        assert np.array_equal(pool.len[slots], oln)
+        kinds.append(mode)
+    assert svt.SVT_COMMIT_APPEND in kinds and svt.SVT_COMMIT_REPAD in kinds   # both paths were taken
+    gkm = _host_rows(pool.kv, km.shape)
+    gtm, gpos = H.from_dev(pool.tokens), H.from_dev(pool.pos)
+    for s in range(P):
+        a, e = pool.end[s] - pool.len[s], pool.end[s]
+        assert np.array_equal(gkm[:, :, s, :, a:e], km[:, :, s, :, a:e]), f"slot {s}"
+        assert np.array_equal(gtm[s, a:e], tm[s, a:e]), f"tokens slot {s}"
+        if a or e != lens0[s]:   # rows that some call wrote position ids for
+            assert np.array_equal(gpos[s, :e], opos[s, :e]), f"pos slot {s}"
