@@ -44,6 +44,9 @@ def parse():
                     help="measure the realignment overhead of EQSPEC (fixed batch, re-pad every round) against "
                          "EXSPEC (sequence pool, equal-length batches append) instead of the round benchmark")
     ap.add_argument("--sched-rounds", type=int, default=24)
+    ap.add_argument("--sweep", action="store_true",
+                    help="cost of one round against the tree budget: M in {8..255} x depth in {4..10} on the "
+                         "B=32 workload's shapes, instead of the round benchmark")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -292,6 +295,100 @@ def sched_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def sweep_bench(args):
+    """Round cost against the tree budget: for M draft nodes and a depth cap,
+    layered trees (nodes spread evenly over the levels) on the B=32 workload's
+    shapes (prefix U[1024, 8192], GQA 32/8, D=128, V=32000, 36 layers).  Per
+    call times from HIP events over 5 steps after 2 warm-up steps; every step
+    restores the lengths, so it moves the same bytes.  Prints one JSON line."""
+    import torch
+    from synth import gen
+    from synth import workloads as wl
+    from tree_masked_verification_parent_amd import svt
+    from tree_masked_verification_parent_amd.round import VerifyRound
+
+    w = wl.workload(4)
+    L = w.layers
+    lens0 = wl.lengths(w)
+    lmax0 = int(lens0.max())
+    dev = torch.device("cuda")
+    gen_t = torch.Generator(device=dev)
+    gen_t.manual_seed(w.seed)
+    len0 = torch.from_numpy(lens0).to(dev)
+    stream = torch.cuda.current_stream()
+    steps, warm = 5, 2
+    rows = []
+    for M in (8, 16, 32, 64, 128, 255):
+        T = M + 1
+        cap = lmax0 + T + 64
+        r = VerifyRound(w.B, M, w.Hq, w.Hkv, w.D, w.V, cap, L, torch.bfloat16, attn_layers=L)
+        for layer in range(L):
+            r.kv_main[layer].normal_(0.0, w.qkv_sigma, generator=gen_t)
+            r.kv_branch[layer].normal_(0.0, w.qkv_sigma, generator=gen_t)
+            r.q[layer].normal_(0.0, w.qkv_sigma, generator=gen_t)
+        logits, des = gen.logits_with_designated_top(gen.stream_key(w.seed, 900, M), w.B * T, w.V)
+        r.logits.copy_(torch.from_numpy(logits.reshape(w.B, T, w.V)))
+        des = des.reshape(w.B, T)
+        del logits
+        for depth in sorted({min(d, M) for d in (4, 6, 8, 10)}):
+            par = np.stack([gen.tree_layered(gen.stream_key(w.seed, 901, M, depth, b), M, depth)
+                            for b in range(w.B)]).astype(np.int32)
+            tok = np.stack([gen.plant_drafts(gen.stream_key(w.seed, 902, M, depth, b), par[b], des[b], w.V,
+                                             w.p_plant) for b in range(w.B)]).astype(np.int32)
+            r.parents.copy_(torch.from_numpy(par))
+            r.tree_tokens.copy_(torch.from_numpy(tok))
+            r.len.copy_(len0)
+            r.lmax.fill_(lmax0)
+            r.set_lmax_bound(lmax0)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+            for k in range(warm + steps):
+                r.len.copy_(len0)
+                r.lmax.fill_(lmax0)
+                ev = evs[k - warm] if k >= warm else None
+                if ev:
+                    ev[0].record(stream)
+                rc = r.build_mask()
+                if ev:
+                    ev[1].record(stream)
+                for layer in range(L):
+                    rc = rc or r.attention(layer)
+                if ev:
+                    ev[2].record(stream)
+                rc = rc or r.accept()
+                if ev:
+                    ev[3].record(stream)
+                rc = rc or r.commit()
+                if ev:
+                    ev[4].record(stream)
+                assert rc == 0, (M, depth, rc)
+            torch.cuda.synchronize()
+            assert r.commit_status.item() == 0 and (r.status.cpu().numpy() == 0).all()
+            A = r.accept_len.cpu().numpy() + 1
+
+            def dur(i, j):
+                return float(np.median([e[i].elapsed_time(e[j]) for e in evs])) * 1e3
+
+            t = {"mask_us": dur(0, 1), "attn_us": dur(1, 2), "accept_us": dur(2, 3), "commit_us": dur(3, 4)}
+            t_round = sum(t.values())
+            rows.append({"M": M, "depth": depth, **t, "attn_us_per_layer": t["attn_us"] / L,
+                         "round_us": t_round, "mean_accept_len": float(np.mean(A - 1)),
+                         "us_per_verified_node": t_round / (w.B * M),
+                         "us_per_accepted_token": t_round / float(A.sum())})
+            print(f"[sweep] M={M:3d} depth={depth:2d}: round {t_round:8.1f} us (mask {t['mask_us']:.1f}, "
+                  f"attention {t['attn_us'] / L:.1f}/layer, accept {t['accept_us']:.1f}, commit "
+                  f"{t['commit_us']:.1f}); accept_len {np.mean(A - 1):.2f}; "
+                  f"{t_round / float(A.sum()):.2f} us per accepted token", file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
+    out = {"metric": "verification round cost against tree budget (M, depth)", "unit": "us per round",
+           "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+           "data": "synthetic (layered trees, planted drafts p=%.2f, seeded logits; device-seeded normal caches)"
+                   % w.p_plant,
+           "config": {"workload": w.name + " shapes, budget sweep", "layers": L, "steps": steps, "warmup": warm},
+           "results": rows}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -300,6 +397,9 @@ def main():
         sys.exit(2)
     if args.sched:
         sched_bench(args)
+        return
+    if args.sweep:
+        sweep_bench(args)
         return
 
     import torch

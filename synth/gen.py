@@ -156,6 +156,26 @@ def tree_depth_capped(key, M: int, depth_cap: int) -> np.ndarray:
     return par
 
 
+def tree_layered(key, M: int, depth: int) -> np.ndarray:
+    """M nodes spread as evenly as possible over levels 1..min(depth, M) (lower
+    levels take the remainder); a node picks its parent uniformly among the
+    nodes of the level above (the root is level 0).  Node ids grow with level."""
+    D = max(1, min(depth, M))
+    per = [M // D + (1 if k < M % D else 0) for k in range(D)]
+    par = np.zeros(M + 1, dtype=np.int32)
+    u = uniform01(key, max(M, 1))
+    prev = [0]
+    i = 1
+    for k in range(D):
+        cur = []
+        for _ in range(per[k]):
+            par[i] = prev[min(int(u[i - 1] * len(prev)), len(prev) - 1)]
+            cur.append(i)
+            i += 1
+        prev = cur
+    return par
+
+
 def tree_bushy(key, M: int, depth_cap: int = 10, wide: int = 4, narrow: int = 2,
                wide_depth: int = 1) -> np.ndarray:
     """Wide near the root: a node of depth <= wide_depth takes up to `wide`

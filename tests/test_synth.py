@@ -1,6 +1,7 @@
 """The input generators: published reference values and cross-implementation
 agreement (C core, numpy, torch)."""
 import numpy as np
+import pytest
 import torch
 
 from synth import gen
@@ -60,3 +61,16 @@ def test_logits_designated_top_is_argmax():
     x, des = gen.logits_with_designated_top(gen.stream_key(11), 50, 3000)
     assert (np.argmax(x, axis=1) == des).all()
     assert np.abs(np.delete(x, des + 3000 * np.arange(50))).max() <= 6.0
+
+
+@pytest.mark.parametrize("M,depth", [(8, 4), (16, 10), (32, 10), (255, 6), (5, 10), (1, 1)])
+def test_layered_trees(M, depth):
+    par = gen.tree_layered(gen.stream_key(123, M, depth), M, depth)
+    lvl = np.zeros(M + 1, np.int64)
+    for i in range(1, M + 1):
+        assert par[i] < i
+        lvl[i] = lvl[par[i]] + 1
+    D = min(depth, M)
+    assert lvl.max() == D
+    counts = np.bincount(lvl[1:], minlength=D + 1)[1:]
+    assert counts.max() - counts.min() <= 1 and counts.sum() == M
