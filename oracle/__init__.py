@@ -56,6 +56,8 @@ def lib():
         L.oracle_commit.restype = ctypes.c_int
         L.oracle_realign.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, i32, P, P, P]
         L.oracle_realign.restype = ctypes.c_int
+        L.oracle_expand_mask.argtypes = [P, P, P, i32, i32, i32, P, P]
+        L.oracle_expand_mask.restype = None
         _lib = L
     return _lib
 
@@ -143,7 +145,8 @@ def commit(kv_main: np.ndarray, kv_branch: np.ndarray, M: int, tokens_main, tree
            lmax: int, path, accept_len, status=None, want_pos_ids: bool = True, mode: int = 0, slot=None):
     """kv_main [L][2][rows][Hkv][cap][...] and kv_branch [L][2][B][Hkv][T][...] of
     any dtype (raw bytes are moved); rows = B unless `slot` maps each sequence
-    to a pool row.  mode 0 re-pads (EQSPEC), 1 appends (EXSPEC).  Works on
+    to a pool row.  mode 0 re-pads (EQSPEC), 1 appends (EXSPEC).  path None is
+    the length-based commit (branch rows [0, A) in step order).  Works on
     copies; returns (rc, kv_main', tokens_main', lens', lmax', pos_ids)."""
     km = np.array(kv_main, copy=True, order="C")
     kb = _c(kv_branch, kv_branch.dtype)
@@ -158,7 +161,7 @@ def commit(kv_main: np.ndarray, kv_branch: np.ndarray, M: int, tokens_main, tree
     st = None if status is None else _c(status, np.int32)
     sl = None if slot is None else _c(slot, np.int32)
     rc = lib().oracle_commit(_p(km.view(np.uint8)), _p(kb.view(np.uint8)), L, B, Hkv, cap, row_bytes, M,
-                             _p(tm), _p(tt), _p(ln), _p(lm), _p(pos), _p(_c(path, np.int32)),
+                             _p(tm), _p(tt), _p(ln), _p(lm), _p(pos), _p(None if path is None else _c(path, np.int32)),
                              _p(_c(accept_len, np.int32)), _p(st), int(mode), _p(sl), rows)
     return rc, km, tm, ln, int(lm[0]), pos
 
@@ -178,3 +181,14 @@ def realign(kv_main: np.ndarray, lens, ends, tokens_main=None, slot=None, want_p
     rc = lib().oracle_realign(_p(km.view(np.uint8)), L, B, Hkv, cap, row_bytes, _p(tm), _p(pos), _p(sl), rows,
                               _p(_c(lens, np.int32)), _p(_c(ends, np.int32)), _p(lm))
     return rc, km, tm, int(lm[0]), pos
+
+
+def expand_mask(parents, lens, lmax: int, status=None):
+    """Dense tree mask from the parent arrays: (codes [B], open [B][T][lmax+T] bool)."""
+    par = _c(parents, np.int32)
+    B, T = par.shape
+    openm = np.zeros((B, T, lmax + T), dtype=np.uint8)
+    codes = np.zeros(B, dtype=np.int32)
+    lib().oracle_expand_mask(_p(par), _p(_c(lens, np.int32)), _p(None if status is None else _c(status, np.int32)),
+                             B, T - 1, int(lmax), _p(openm), _p(codes))
+    return codes, openm.astype(bool)

@@ -271,6 +271,12 @@ void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_
 /* ------------------------------------------------------------------------ */
 static int slot_of(const int32_t* slot, int32_t b) { return slot ? slot[b] : b; }
 
+/* Branch row of accepted step k of sequence b: the path entry, or k itself
+ * for the length-based commit of [EP-nl] §2.A (no path given). */
+static int32_t step_row(const int32_t* path, int32_t T, int32_t b, int32_t k) {
+  return path ? path[(int64_t)b * T + k] : k;
+}
+
 int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, int32_t B,
                   int32_t Hkv, int64_t cap, int32_t row_bytes, int32_t M,
                   int32_t* tokens_main, const int32_t* tree_tokens, int32_t* len, int32_t* lmax,
@@ -299,7 +305,7 @@ int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, 
       } else {
         A[b] = accept_len[b] + 1;
         for (int32_t k = 0; k < A[b]; ++k)
-          if (path[(int64_t)b * T + k] < 0 || path[(int64_t)b * T + k] > M) arg_bad = 1;
+          if (step_row(path, T, b, k) < 0 || step_row(path, T, b, k) > M) arg_bad = 1;
       }
     }
     int32_t new_end = mode == 1 ? old_lmax + A[b] : len[b] + A[b];
@@ -326,7 +332,7 @@ int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, 
           for (int32_t c = old_lmax - len[b]; c < old_lmax; ++c, ++n)
             memcpy(tmp + (int64_t)n * row_bytes, main_s + (int64_t)c * row_bytes, (size_t)row_bytes);
           for (int32_t k = 0; k < A[b]; ++k, ++n)
-            memcpy(tmp + (int64_t)n * row_bytes, br_s + (int64_t)path[(int64_t)b * T + k] * row_bytes,
+            memcpy(tmp + (int64_t)n * row_bytes, br_s + (int64_t)step_row(path, T, b, k) * row_bytes,
                    (size_t)row_bytes);
           memcpy(main_s + (int64_t)start[b] * row_bytes, tmp, (size_t)n * (size_t)row_bytes);
         }
@@ -341,7 +347,7 @@ int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, 
       int32_t n = 0;
       for (int32_t c = old_lmax - len[b]; c < old_lmax; ++c) ttmp[n++] = tm[c];
       for (int32_t k = 0; k < A[b]; ++k)
-        ttmp[n++] = tree_tokens[(int64_t)b * T + path[(int64_t)b * T + k]];
+        ttmp[n++] = tree_tokens[(int64_t)b * T + step_row(path, T, b, k)];
       for (int32_t x = 0; x < n; ++x) tm[start[b] + x] = ttmp[x];
     }
     if (pos_ids) {
@@ -401,4 +407,34 @@ int oracle_realign(uint8_t* kv_main, int32_t n_layers, int32_t B, int32_t Hkv, i
   free(ttmp);
   *lmax = E;
   return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense tree mask.  [EP-nl] §2.C: token k attends token j only when j is an */
+/* ancestor of k (here: or k itself); the prefix is visible to every node.   */
+/* Each node's chain is walked from the parent array, independently of the   */
+/* bitmask that oracle_mask builds.                                          */
+/* ------------------------------------------------------------------------ */
+void oracle_expand_mask(const int32_t* parents, const int32_t* len, const int32_t* status, int32_t B,
+                        int32_t M, int32_t lmax, uint8_t* open, int32_t* code) {
+  int32_t T = M + 1;
+  int64_t width = (int64_t)lmax + T;
+  memset(open, 0, (size_t)B * (size_t)T * (size_t)width);
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t st = status ? status[b] : 0;
+    code[b] = st != 0 ? st : ((len[b] >= 0 && len[b] <= lmax) ? 0 : ORACLE_ERR_LENGTH);
+    if (code[b] != 0) continue;
+    const int32_t* par = parents + (int64_t)b * T;
+    for (int32_t i = 0; i < T; ++i) {
+      uint8_t* row = open + ((int64_t)b * T + i) * width;
+      for (int64_t c = lmax - len[b]; c < lmax; ++c) row[c] = 1;
+      /* the node itself, then every ancestor up to the root */
+      int32_t u = i;
+      row[lmax + u] = 1;
+      for (int32_t steps = 0; u != 0 && steps <= M; ++steps) {
+        u = par[u];
+        row[lmax + u] = 1;
+      }
+    }
+  }
 }

@@ -48,6 +48,18 @@ int oracle_validate(const int32_t* parents, int32_t B, int32_t M, int32_t* statu
 void oracle_mask(const int32_t* parents, int32_t B, int32_t M, const int32_t* status,
                  uint64_t* mask, int32_t* depth);
 
+/* Dense 4D tree mask for eager attention ([EP-nl] §2.C: token k may attend
+ * token j only when j is an ancestor of k; reference mode with the fused
+ * attention off; [EP-ko] §2 4D tree attention mask).  Computed from the
+ * parent arrays by walking each node's chain (reflexive reading).
+ *   open [B][T][lmax + T] out: 1 where row i of sequence b may attend the
+ *   column, else 0.  Columns c < lmax are the left-padded prefix (content
+ *   from lmax - len_b), columns lmax + j the tree nodes.  A sequence with a
+ *   nonzero status or len_b outside [0, lmax] gets all zeros; code [B] out
+ *   receives 0, its status, or ORACLE_ERR_LENGTH.  status may be NULL. */
+void oracle_expand_mask(const int32_t* parents, const int32_t* len, const int32_t* status, int32_t B,
+                        int32_t M, int32_t lmax, uint8_t* open, int32_t* code);
+
 /* Tree-verify attention ([EP-ko] §2 fused tree-masked teacher execution;
  * [EP-nl] §2.C).  All tensors are float (exact upcasts of what the GPU reads);
  * the result is double.
@@ -93,6 +105,8 @@ void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_
  *   slot [B] or NULL: sequence b is row slot[b] of kv_main, tokens_main and
  *   pos_ids (rows = B when NULL)
  *   mode 0 = re-pad (EQSPEC), 1 = append without moving (EXSPEC)
+ *   path NULL: length-based commit ([EP-nl] §2.A): step k of the chosen
+ *   branch is branch row k, so rows [0, A_b) are appended
  * Returns 0, or on error (nothing changes) ORACLE_ERR_LENGTH for inconsistent
  * lengths, ORACLE_ERR_ARG for an accept length or path entry outside [0, M]
  * or a slot outside [0, rows), ORACLE_ERR_CAPACITY when a sequence would end
