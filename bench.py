@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="cost of one round against the tree budget: M in {8..255} x depth in {4..10} on the "
                          "B=32 workload's shapes, instead of the round benchmark")
+    ap.add_argument("--interop", action="store_true",
+                    help="time the reference-mode calls (dense 4D mask expansion, length-based commit) on the "
+                         "B=32 workload instead of the round benchmark")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -389,6 +392,84 @@ def sweep_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def interop_bench(args):
+    """svt_expand_mask (three output kinds) and svt_commit_length against
+    svt_commit on the B=32 workload (M=32, prefix U[1024, 8192], 36 layers).
+    HIP events over 20 calls after 3 warm-up calls; the commit calls restore
+    the lengths before each call.  Prints one JSON line."""
+    import torch
+    from synth import workloads as wl
+    from tree_masked_verification_parent_amd import svt
+    from tree_masked_verification_parent_amd.round import VerifyRound
+
+    w = wl.workload(4)
+    dev = torch.device("cuda")
+    parents = wl.trees(w)
+    lens0 = wl.lengths(w)
+    lmax0 = int(lens0.max())
+    logits, tokens, _ = wl.logits_and_drafts(w, parents)
+    L = w.layers
+    r = VerifyRound(w.B, w.M, w.Hq, w.Hkv, w.D, w.V, lmax0 + w.T + 64, L, torch.bfloat16, attn_layers=1)
+    gen_t = torch.Generator(device=dev)
+    gen_t.manual_seed(w.seed)
+    for layer in range(L):
+        r.kv_main[layer].normal_(0.0, w.qkv_sigma, generator=gen_t)
+        r.kv_branch[layer].normal_(0.0, w.qkv_sigma, generator=gen_t)
+    r.parents.copy_(torch.from_numpy(parents))
+    r.tree_tokens.copy_(torch.from_numpy(tokens))
+    r.logits.copy_(torch.from_numpy(logits))
+    len0 = torch.from_numpy(lens0).to(dev)
+    r.len.copy_(len0)
+    r.lmax.fill_(lmax0)
+    r.set_lmax_bound(lmax0)
+    assert r.build_mask(svt.SVT_SYNC_CHECK) == 0 and r.accept() == 0
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n, warm = 20, 3
+
+    def timed(fn, before=None):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for k in range(warm + n):
+            if before:
+                before()
+            if k >= warm:
+                evs[k - warm][0].record(stream)
+            assert fn() == 0
+            if k >= warm:
+                evs[k - warm][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    res = {}
+    T = w.T
+    for kind, dt, name in [(svt.SVT_MASK_ADD_FP32, torch.float32, "add_fp32"),
+                           (svt.SVT_MASK_ADD_BF16, torch.bfloat16, "add_bf16"), (svt.SVT_MASK_BOOL, torch.uint8, "bool")]:
+        out = torch.empty(w.B, 1, T, lmax0 + T, dtype=dt, device=dev)
+        us = timed(lambda: svt.svt_expand_mask(r.mask, r.status, r.len, w.M, lmax0, out, kind))
+        nbytes = out.numel() * out.element_size()
+        res["expand_" + name] = {"us": us, "bytes_written": nbytes, "GBps": nbytes / us / 1e3,
+                                 "frac_hbm": nbytes / us / 1e3 / HBM_PEAK_GBPS}
+        del out
+
+    def restore():
+        r.len.copy_(len0)
+        r.lmax.fill_(lmax0)
+
+    us_path = timed(lambda: svt.svt_commit(r._commit_args()), restore)
+    us_len = timed(lambda: svt.svt_commit_length(r._commit_args()), restore)
+    A = r.accept_len.cpu().numpy().astype(np.int64) + 1
+    cbytes = algorithmic_bytes_commit(w, lens0, A, L)
+    res["commit_path_us"] = us_path
+    res["commit_length_us"] = us_len
+    res["commit_GBps"] = {"path": cbytes / us_path / 1e3, "length": cbytes / us_len / 1e3}
+    out = {"metric": "reference-mode interop: dense 4D mask expansion GB/s, length-based commit us",
+           "unit": "see fields", "n_gpus": 1, "dtype": "bf16", "data": "synthetic (B=32 ragged workload)",
+           "config": {"workload": w.name, "lmax": lmax0, "T": T, "layers": L}, "results": res}
+    for k, v in res.items():
+        print(f"[interop] {k}: {v}", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -400,6 +481,9 @@ def main():
         return
     if args.sweep:
         sweep_bench(args)
+        return
+    if args.interop:
+        interop_bench(args)
         return
 
     import torch

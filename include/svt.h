@@ -11,7 +11,8 @@
  *
  * plus svt_realign (bring a batch drawn from a sequence pool to a common end
  * column) and svt_pool_pick (host: choose the next batch from a pool) for
- * cross-batch scheduling.
+ * cross-batch scheduling, svt_expand_mask (dense 4D mask for eager attention
+ * paths) and svt_commit_length (length-based commit).
  *
  * Sources (summary pages of two papers):
  *   [EP-ko] "EAGLE-Pangu: Accelerator-Safe Tree Speculative Decoding on Ascend
@@ -92,6 +93,31 @@ typedef enum svt_dtype { SVT_FP32 = 0, SVT_BF16 = 1 } svt_dtype;
 /* ------------------------------------------------------------------------ */
 int svt_build_mask(const int32_t* parents, int32_t B, int32_t M, uint64_t* mask, int32_t* depth,
                    int32_t* status, int32_t flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* svt_expand_mask                                                           */
+/* Dense 4D tree mask for eager attention paths ([EP-nl] section 2.C: a 4D    */
+/* mask lets token k attend token j only when j is an ancestor of k; the      */
+/* reference mode runs with the fused attention switched off; [EP-ko]         */
+/* section 2: 4D tree attention mask, eager and performance modes).           */
+/*   out[b][0][i][c], c < lmax + T: prefix column c < lmax is open when it     */
+/*   holds content (c >= lmax - len[b], left padding); tree column lmax + j    */
+/*   is open when bit j of mask[b][i] is set (j is i or an ancestor of i).     */
+/*   Open = 0 and closed = -inf for the additive kinds (fp32, or bf16 bits);   */
+/*   open = 1 and closed = 0 for SVT_MASK_BOOL (uint8).  The key order is the  */
+/*   one of svt_verify_attention: lmax cache columns, then the T tree rows.    */
+/*   A sequence with a nonzero status[b] or len[b] outside [0, lmax] gets      */
+/*   every column closed; seq_status[b] (if given) receives SVT_OK, the tree   */
+/*   status or SVT_ERR_LENGTH.                                                 */
+/* Arguments: mask [B][T][W] from svt_build_mask; status [B] or NULL; len [B] */
+/* device; lmax host (prefix columns, >= 0); out [B][1][T][lmax + T] of the   */
+/* kind's element (4, 2 or 1 bytes).  Returns SVT_OK, SVT_ERR_ARG /           */
+/* SVT_ERR_UNSUPPORTED (host) or SVT_ERR_HIP.                                 */
+/* ------------------------------------------------------------------------ */
+typedef enum svt_mask_kind { SVT_MASK_ADD_FP32 = 0, SVT_MASK_ADD_BF16 = 1, SVT_MASK_BOOL = 2 } svt_mask_kind;
+
+int svt_expand_mask(const uint64_t* mask, const int32_t* status, const int32_t* len, int32_t B, int32_t M,
+                    int32_t lmax, void* out, int32_t kind, int32_t* seq_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* svt_verify_attention                                                      */
@@ -249,6 +275,14 @@ typedef struct svt_commit_args {
 typedef enum svt_commit_mode { SVT_COMMIT_REPAD = 0, SVT_COMMIT_APPEND = 1 } svt_commit_mode;
 
 int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream);
+
+/* svt_commit_length: the length-based commit of [EP-nl] section 2.A (keep the */
+/* prefix, append the first A steps of the chosen branch).  kv_branch and      */
+/* tree_tokens hold each sequence's chosen branch in step order (row k = step  */
+/* k, row 0 the root); rows [0, A_b) are committed, A_b = accept_len[b] + 1.   */
+/* Everything else, modes and errors included, is svt_commit with path[b][k]   */
+/* = k; a->path is ignored (may be NULL).                                      */
+int svt_commit_length(const svt_commit_args* a, int32_t flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* svt_realign                                                               */

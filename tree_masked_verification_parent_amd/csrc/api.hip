@@ -44,6 +44,20 @@ int svt_build_mask(const int32_t* parents, int32_t B, int32_t M, uint64_t* mask,
   return finish("svt_build_mask", rc, shape);
 }
 
+int svt_expand_mask(const uint64_t* mask, const int32_t* status, const int32_t* len, int32_t B, int32_t M,
+                    int32_t lmax, void* out, int32_t kind, int32_t* seq_status, hipStream_t stream) {
+  char shape[96];
+  std::snprintf(shape, sizeof shape, "B=%d M=%d lmax=%d kind=%d", B, M, lmax, kind);
+  if (B < 0 || M < 0 || lmax < 0 || kind < SVT_MASK_ADD_FP32 || kind > SVT_MASK_BOOL)
+    return finish("svt_expand_mask", SVT_ERR_ARG, shape);
+  if (M >= SVT_MAX_T) return finish("svt_expand_mask", SVT_ERR_UNSUPPORTED, shape);
+  if ((int64_t)B * (M + 1) > 65535) return finish("svt_expand_mask", SVT_ERR_UNSUPPORTED, shape);
+  if (B == 0) return finish("svt_expand_mask", SVT_OK, shape);
+  if (!mask || !len || !out || !aligned(mask, 8)) return finish("svt_expand_mask", SVT_ERR_ARG, shape);
+  return finish("svt_expand_mask", hip_rc(svt::launch_expand_mask(mask, status, len, B, M, lmax, out, kind,
+                                                                   seq_status, stream)), shape);
+}
+
 size_t svt_verify_attention_workspace(const svt_attn_args* a) {
   svt::AttnPlan p;
   if (!svt::plan_attention(a, &p)) return 0;
@@ -103,28 +117,37 @@ int svt_accept(const svt_accept_args* a, hipStream_t stream) {
   return finish("svt_accept", hip_rc(svt::launch_accept(a, p, stream)), shape);
 }
 
-int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream) {
+static int commit_impl(const char* name, const svt_commit_args* a, bool by_length, int32_t flags,
+                       hipStream_t stream) {
   char shape[128];
-  if (!a) return finish("svt_commit", SVT_ERR_ARG, "null args");
+  if (!a) return finish(name, SVT_ERR_ARG, "null args");
   std::snprintf(shape, sizeof shape, "B=%d M=%d Hkv=%d D=%d layers=%d dtype=%d cap=%lld mode=%d slots=%d", a->B, a->M,
                 a->Hkv, a->D, a->n_layers, a->dtype, (long long)a->cap, a->mode, a->seq_slot ? a->n_slots : -1);
   if (a->B < 0 || a->M < 0 || a->Hkv < 0 || a->D <= 0 || a->n_layers < 0 || a->cap < 0 || a->cap > 0x7FFFFFFF)
-    return finish("svt_commit", SVT_ERR_ARG, shape);
-  if (a->mode != SVT_COMMIT_REPAD && a->mode != SVT_COMMIT_APPEND) return finish("svt_commit", SVT_ERR_ARG, shape);
-  if (a->seq_slot && a->n_slots <= 0) return finish("svt_commit", SVT_ERR_ARG, shape);
+    return finish(name, SVT_ERR_ARG, shape);
+  if (a->mode != SVT_COMMIT_REPAD && a->mode != SVT_COMMIT_APPEND) return finish(name, SVT_ERR_ARG, shape);
+  if (a->seq_slot && a->n_slots <= 0) return finish(name, SVT_ERR_ARG, shape);
   if (a->M >= SVT_MAX_T || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
-    return finish("svt_commit", SVT_ERR_UNSUPPORTED, shape);
+    return finish(name, SVT_ERR_UNSUPPORTED, shape);
   const int esize = a->dtype == SVT_FP32 ? 4 : 2;
-  if ((a->D * esize) % 16 != 0) return finish("svt_commit", SVT_ERR_UNSUPPORTED, shape);
-  if (!a->len || !a->lmax || !a->path || !a->accept_len || !a->commit_status)
-    return finish("svt_commit", SVT_ERR_ARG, shape);
+  if ((a->D * esize) % 16 != 0) return finish(name, SVT_ERR_UNSUPPORTED, shape);
+  if (!a->len || !a->lmax || (!by_length && !a->path) || !a->accept_len || !a->commit_status)
+    return finish(name, SVT_ERR_ARG, shape);
   const bool has_kv = a->n_layers > 0 && a->Hkv > 0 && a->B > 0;
   if (has_kv && (!a->kv_main || !a->kv_branch || !aligned(a->kv_main, 16) || !aligned(a->kv_branch, 16)))
-    return finish("svt_commit", SVT_ERR_ARG, shape);
-  if (a->tokens_main && !a->tree_tokens) return finish("svt_commit", SVT_ERR_ARG, shape);
-  int rc = hip_rc(svt::launch_commit(a, stream));
+    return finish(name, SVT_ERR_ARG, shape);
+  if (a->tokens_main && !a->tree_tokens) return finish(name, SVT_ERR_ARG, shape);
+  int rc = hip_rc(by_length ? svt::launch_commit_length(a, stream) : svt::launch_commit(a, stream));
   if (rc == SVT_OK && (flags & SVT_SYNC_CHECK)) rc = svt_check_status(a->commit_status, 1, stream);
-  return finish("svt_commit", rc, shape);
+  return finish(name, rc, shape);
+}
+
+int svt_commit(const svt_commit_args* a, int32_t flags, hipStream_t stream) {
+  return commit_impl("svt_commit", a, false, flags, stream);
+}
+
+int svt_commit_length(const svt_commit_args* a, int32_t flags, hipStream_t stream) {
+  return commit_impl("svt_commit_length", a, true, flags, stream);
 }
 
 int svt_realign(const svt_realign_args* a, int32_t flags, hipStream_t stream) {

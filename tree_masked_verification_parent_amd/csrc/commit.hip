@@ -49,7 +49,7 @@ struct CommitDev {
   const int32_t* len;        // [B]
   const int32_t* lmax;       // [1] (commit modes)
   const int32_t* end;        // [B] (realign)
-  const int32_t* path;       // [B][T] (commit modes)
+  const int32_t* path;       // [B][T], or NULL: row k of the branch is step k (length-based)
   const int32_t* acc;        // [B] (commit modes)
   const int32_t* status;     // [B] or NULL
   int32_t* len_out;          // [B] updated in place (commit modes)
@@ -106,7 +106,7 @@ __device__ CommitPlan compute_commit_plan(const CommitDev& d) {
     const int ne = d.mode == kAppend ? old_lmax + A : L + A;
     mx = ne > mx ? ne : mx;
   }
-  if (d.mode != kRealign) {
+  if (d.mode != kRealign && d.path) {
     for (int x = tid; x < d.B * T; x += blockDim.x) {
       const int b = x / T, k = x % T;
       const bool valid = d.status == nullptr || d.status[b] == 0;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void commit_move_kernel(CommitDev d) {
     pend = plan.new_lmax;
   }
   const int tid = threadIdx.x;
-  const int32_t* pb = d.mode == kRealign ? nullptr : d.path + (int64_t)b * T;
+  const int32_t* pb = d.path ? d.path + (int64_t)b * T : nullptr;
 
   if (x < d.n_slab_x) {
     // x = (layer * 2 + plane) * Hkv + h
@@ -202,14 +202,14 @@ __global__ __launch_bounds__(256) void commit_move_kernel(CommitDev d) {
       const int n = A * d.row16;
       for (int i = tid; i < n; i += 256) {
         const int k = i / d.row16, e = i % d.row16;
-        out[i] = br_s[(int64_t)pb[k] * d.row16 + e];
+        out[i] = br_s[(int64_t)(pb ? pb[k] : k) * d.row16 + e];
       }
     }
   } else {
     if (d.tok) {
       int32_t* tm = d.tok + (int64_t)row * d.cap;
       shift_in_place<int32_t, 4>(tm, src, L, (int64_t)dst - src);
-      for (int k = tid; k < A; k += 256) tm[app + k] = d.ttok[(int64_t)b * T + pb[k]];
+      for (int k = tid; k < A; k += 256) tm[app + k] = d.ttok[(int64_t)b * T + (pb ? pb[k] : k)];
     }
     if (d.pos) {
       int32_t* pp = d.pos + (int64_t)row * d.cap;
@@ -264,6 +264,12 @@ hipError_t launch_commit(const svt_commit_args* a, hipStream_t s) {
   d.row16 = a->D * esize / 16;
   d.mode = a->mode;
   return launch_move(d, a->n_layers, s);
+}
+
+hipError_t launch_commit_length(const svt_commit_args* a, hipStream_t s) {
+  svt_commit_args b = *a;
+  b.path = nullptr;
+  return launch_commit(&b, s);
 }
 
 hipError_t launch_realign(const svt_realign_args* a, hipStream_t s) {

@@ -45,6 +45,9 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
 hipError_t launch_accept(const svt_accept_args* a, const AcceptPlan& p, hipStream_t s);
 hipError_t launch_commit(const svt_commit_args* a, hipStream_t s);
 hipError_t launch_realign(const svt_realign_args* a, hipStream_t s);
+hipError_t launch_expand_mask(const uint64_t* mask, const int32_t* status, const int32_t* len, int B, int M,
+                              int P, void* out, int kind, int32_t* seq_status, hipStream_t s);
+hipError_t launch_commit_length(const svt_commit_args* a, hipStream_t s);
 
 // ---- host-only scheduling (pool.cpp) ----
 int pool_pick(const int32_t* end, const int32_t* active, int n_slots, int max_batch, int min_group,

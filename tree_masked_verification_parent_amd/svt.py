@@ -32,6 +32,7 @@ SVT_BF16 = 1
 SVT_SYNC_CHECK = 1
 SVT_ATTN_AUTO, SVT_ATTN_SPLIT, SVT_ATTN_STREAM = 0, 1, 2
 SVT_COMMIT_REPAD, SVT_COMMIT_APPEND = 0, 1
+SVT_MASK_ADD_FP32, SVT_MASK_ADD_BF16, SVT_MASK_BOOL = 0, 1, 2
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -65,9 +66,9 @@ class RealignArgs(ctypes.Structure):
                 ("len", _P), ("end", _P), ("lmax", _P), ("realign_status", _P)]
 
 
-EXPORTS = ["svt_build_mask", "svt_verify_attention_workspace", "svt_verify_attention", "svt_accept_workspace",
-           "svt_accept", "svt_commit", "svt_realign", "svt_pool_pick", "svt_check_status", "svt_status_string",
-           "svt_version"]
+EXPORTS = ["svt_build_mask", "svt_expand_mask", "svt_verify_attention_workspace", "svt_verify_attention",
+           "svt_accept_workspace", "svt_accept", "svt_commit", "svt_commit_length", "svt_realign", "svt_pool_pick",
+           "svt_check_status", "svt_status_string", "svt_version"]
 
 _lib = None
 
@@ -92,6 +93,10 @@ def lib():
         L.svt_accept.restype = ctypes.c_int
         L.svt_commit.argtypes = [ctypes.POINTER(CommitArgs), _I32, _P]
         L.svt_commit.restype = ctypes.c_int
+        L.svt_commit_length.argtypes = [ctypes.POINTER(CommitArgs), _I32, _P]
+        L.svt_commit_length.restype = ctypes.c_int
+        L.svt_expand_mask.argtypes = [_P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P]
+        L.svt_expand_mask.restype = ctypes.c_int
         L.svt_realign.argtypes = [ctypes.POINTER(RealignArgs), _I32, _P]
         L.svt_realign.restype = ctypes.c_int
         L.svt_pool_pick.argtypes = [_P, _P, _I32, _I32, _I32, _P, _P]
@@ -141,6 +146,17 @@ def version() -> str:
 def svt_build_mask(parents, M: int, mask, depth, status, flags: int = 0, stream=None) -> int:
     B = parents.shape[0] if parents.dim() > 1 else 1
     return lib().svt_build_mask(_ptr(parents), B, M, _ptr(mask), _ptr(depth), _ptr(status), flags, _stream(stream))
+
+
+def svt_expand_mask(mask, status, lens, M: int, lmax: int, out, kind: int, seq_status=None, stream=None) -> int:
+    """out: [B][1][T][lmax + T] of float32 (SVT_MASK_ADD_FP32), bfloat16
+    (SVT_MASK_ADD_BF16) or uint8 (SVT_MASK_BOOL)."""
+    B = mask.shape[0]
+    want = {SVT_MASK_ADD_FP32: torch.float32, SVT_MASK_ADD_BF16: torch.bfloat16, SVT_MASK_BOOL: torch.uint8}
+    if kind in want and (out.dtype != want[kind] or out.numel() != B * (M + 1) * (lmax + M + 1)):
+        raise ValueError("out must be [B][1][T][lmax + T] of the kind's dtype")
+    return lib().svt_expand_mask(_ptr(mask), _ptr(status), _ptr(lens), B, M, int(lmax), _ptr(out), int(kind),
+                                 _ptr(seq_status), _stream(stream))
 
 
 def _dtype_code(t):
@@ -223,6 +239,10 @@ def commit_args(kv_main, kv_branch, lens, lmax, path, accept_len, commit_status,
 
 def svt_commit(args: CommitArgs, flags: int = 0, stream=None) -> int:
     return lib().svt_commit(ctypes.byref(args), flags, _stream(stream))
+
+
+def svt_commit_length(args: CommitArgs, flags: int = 0, stream=None) -> int:
+    return lib().svt_commit_length(ctypes.byref(args), flags, _stream(stream))
 
 
 def svt_check_status(status, n: int, stream=None) -> int:
