@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--interop", action="store_true",
                     help="time the reference-mode calls (dense 4D mask expansion, length-based commit) on the "
                          "B=32 workload instead of the round benchmark")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="round time of the B=32 workload with the commit of each round overlapped layer by layer "
+                         "with the next round's attention (eager and HIP graph) against sequential rounds")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -470,6 +473,97 @@ def interop_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def pipeline_bench(args):
+    """Steady-state round time of the B=32 workload (36 layers): sequential
+    rounds (verify, then a 36-layer commit) against rounds whose commit runs
+    layer by layer on a second stream while the next round's attention waits
+    only for its own layer, eager and replayed from HIP graphs.  The two
+    buffer sets carry different trees, drafts and logits, so the accept
+    lengths differ between rounds and the commits move data.  Prints one
+    JSON line."""
+    import torch
+    from synth import workloads as wl
+    from tree_masked_verification_parent_amd import svt
+    from tree_masked_verification_parent_amd.pipeline import RoundPipeline
+
+    w = wl.workload(4)
+    L, R, warm = w.layers, 8, 2
+    lens0 = wl.lengths(w)
+    lmax0 = int(lens0.max())
+    cap = lmax0 + (4 * (R + warm) + 8) * w.T + 64
+    dev = torch.device("cuda")
+    p = RoundPipeline(w.B, w.M, w.Hq, w.Hkv, w.D, w.V, cap, L, torch.bfloat16)
+    gen_t = torch.Generator(device=dev)
+    gen_t.manual_seed(w.seed)
+    for layer in range(L):
+        p.kv_main[layer].normal_(0.0, w.qkv_sigma, generator=gen_t)
+    for si, st in enumerate(p.sets):
+        par = wl.trees(w, w.seed + 10 + si)
+        logits, tokens, _ = wl.logits_and_drafts(w, par, w.seed + 10 + si)
+        st.parents.copy_(torch.from_numpy(par))
+        st.tree_tokens.copy_(torch.from_numpy(tokens))
+        st.logits.copy_(torch.from_numpy(logits))
+        st.q.normal_(0.0, w.qkv_sigma, generator=gen_t)
+        st.kv_branch.normal_(0.0, w.qkv_sigma, generator=gen_t)
+    p.lens[0].copy_(torch.from_numpy(lens0))
+    p.lmax[0].fill_(lmax0)
+    p.set_lmax_bound(cap)
+    stream = torch.cuda.current_stream()
+
+    def run(step, k0, n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record(stream)
+        for i in range(n):
+            assert step(k0 + i) == 0
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        assert p.commit_status.item() == 0
+        return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+
+    k = 0
+    run(p.sequential_step, k, warm)
+    k += warm
+    t_seq = run(p.sequential_step, k, R)
+    k += R
+    assert p.verify(k) == 0                  # verified, not committed: the next pipelined step commits it
+    k += 1
+    run(p.pipelined_step, k, warm)
+    k += warm
+    t_pip = run(p.pipelined_step, k, R)
+    k += R
+    p.attn_form = svt.SVT_ATTN_SPLIT         # the split form schedules many small workgroups
+    p.set_lmax_bound(cap)
+    t_pip_split = run(p.pipelined_step, k, R)
+    k += R
+    p.attn_form = svt.SVT_ATTN_AUTO
+    p.set_lmax_bound(cap)
+    graphs = {0: p.capture(k + (k % 2)), 1: p.capture(k + 1 - (k % 2))}
+
+    def replay(kk):
+        graphs[kk % 2].replay()
+        return 0
+
+    run(replay, k, warm)
+    k += warm
+    t_gra = run(replay, k, R)
+    k += R
+    assert p.commit(k - 1) == 0
+    torch.cuda.synchronize()
+    res = {"sequential_ms": float(np.median(t_seq)), "pipelined_ms": float(np.median(t_pip)),
+           "pipelined_split_attention_ms": float(np.median(t_pip_split)),
+           "pipelined_graph_ms": float(np.median(t_gra))}
+    res["speedup_pipelined"] = res["sequential_ms"] / res["pipelined_ms"]
+    res["speedup_graph"] = res["sequential_ms"] / res["pipelined_graph_ms"]
+    out = {"metric": "verification round time, sequential vs commit overlapped with the next round's attention",
+           "unit": "ms per round", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+           "data": "synthetic (two alternating seeded rounds; device-seeded normal caches)",
+           "config": {"workload": w.name, "layers": L, "rounds": R, "warmup": warm}, "results": res,
+           "per_round_ms": {"sequential": t_seq, "pipelined": t_pip, "pipelined_split_attention": t_pip_split,
+                            "pipelined_graph": t_gra}}
+    print(f"[pipeline] {res}", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -484,6 +578,9 @@ def main():
         return
     if args.interop:
         interop_bench(args)
+        return
+    if args.pipeline:
+        pipeline_bench(args)
         return
 
     import torch

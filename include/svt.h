@@ -239,6 +239,11 @@ int svt_accept(const svt_accept_args* a, hipStream_t stream);
 /* ends at lmax + A_b (the batch stays rectangular only where A_b = max A).  */
 /* pos_ids[b][c] = c - (lmax - len_b) on content, 0 on padding, for           */
 /* c < lmax + A_b.  SVT_ERR_CAPACITY when lmax + A_b > cap for some b.        */
+/* With len_out and lmax_out set, len and lmax are only read, so the same     */
+/* commit can be issued in parts (say one layer at a time, kv_main and        */
+/* kv_branch pointing at that layer, n_layers = 1, with tokens_main and        */
+/* pos_ids given to one of the calls): every call derives the same plan and   */
+/* writes the same len_out, lmax_out and commit_status.                       */
 /* With seq_slot set, sequence b lives in row seq_slot[b] of kv_main,         */
 /* tokens_main and pos_ids (pools of n_slots rows; kv_branch, tree_tokens,    */
 /* len, path, accept_len stay indexed by b).  The slots must be distinct; one */
@@ -270,6 +275,8 @@ typedef struct svt_commit_args {
   const int32_t* seq_slot;     /* [B] pool row of each sequence, or NULL (row b)     */
   int32_t n_slots;             /* pool rows when seq_slot is set                     */
   int32_t mode;                /* svt_commit_mode                                    */
+  int32_t* len_out;            /* [B] new lengths, or NULL: len is updated in place   */
+  int32_t* lmax_out;           /* [1] new lmax, or NULL: lmax is updated in place     */
 } svt_commit_args;
 
 typedef enum svt_commit_mode { SVT_COMMIT_REPAD = 0, SVT_COMMIT_APPEND = 1 } svt_commit_mode;

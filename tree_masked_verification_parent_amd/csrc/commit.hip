@@ -52,7 +52,7 @@ struct CommitDev {
   const int32_t* path;       // [B][T], or NULL: row k of the branch is step k (length-based)
   const int32_t* acc;        // [B] (commit modes)
   const int32_t* status;     // [B] or NULL
-  int32_t* len_out;          // [B] updated in place (commit modes)
+  int32_t* len_out;          // [B] new lengths (commit modes): len itself or a separate array
   int32_t* lmax_out;         // [1]
   int32_t* status_out;       // [1]
   int64_t cap;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void commit_finalize_kernel(CommitDev d) {
   if (threadIdx.x == 0) d.status_out[0] = plan.code;
   if (plan.code != SVT_OK) return;
   if (d.mode != kRealign)
-    for (int b = threadIdx.x; b < d.B; b += blockDim.x) d.len_out[b] += accepted_rows(d, b);
+    for (int b = threadIdx.x; b < d.B; b += blockDim.x) d.len_out[b] = d.len[b] + accepted_rows(d, b);
   if (threadIdx.x == 0) *d.lmax_out = plan.new_lmax;
 }
 
@@ -253,8 +253,8 @@ hipError_t launch_commit(const svt_commit_args* a, hipStream_t s) {
   d.path = a->path;
   d.acc = a->accept_len;
   d.status = a->status;
-  d.len_out = a->len;
-  d.lmax_out = a->lmax;
+  d.len_out = a->len_out ? a->len_out : a->len;
+  d.lmax_out = a->lmax_out ? a->lmax_out : a->lmax;
   d.status_out = a->commit_status;
   d.cap = a->cap;
   d.B = a->B;

@@ -57,7 +57,8 @@ class CommitArgs(ctypes.Structure):
     _fields_ = [("B", _I32), ("M", _I32), ("Hkv", _I32), ("D", _I32), ("n_layers", _I32), ("dtype", _I32),
                 ("cap", _I64), ("kv_main", _P), ("kv_branch", _P), ("tokens_main", _P), ("tree_tokens", _P),
                 ("len", _P), ("lmax", _P), ("pos_ids", _P), ("path", _P), ("accept_len", _P), ("status", _P),
-                ("commit_status", _P), ("seq_slot", _P), ("n_slots", _I32), ("mode", _I32)]
+                ("commit_status", _P), ("seq_slot", _P), ("n_slots", _I32), ("mode", _I32), ("len_out", _P),
+                ("lmax_out", _P)]
 
 
 class RealignArgs(ctypes.Structure):
@@ -217,7 +218,8 @@ def svt_accept(args: AcceptArgs, stream=None) -> int:
 
 
 def commit_args(kv_main, kv_branch, lens, lmax, path, accept_len, commit_status, tokens_main=None,
-                tree_tokens=None, pos_ids=None, status=None, seq_slot=None, mode: int = SVT_COMMIT_REPAD) -> CommitArgs:
+                tree_tokens=None, pos_ids=None, status=None, seq_slot=None, mode: int = SVT_COMMIT_REPAD,
+                len_out=None, lmax_out=None) -> CommitArgs:
     Lyr, two, rows, Hkv, cap, D = kv_main.shape
     B = kv_branch.shape[2]
     if seq_slot is None and rows != B:
@@ -233,8 +235,9 @@ def commit_args(kv_main, kv_branch, lens, lmax, path, accept_len, commit_status,
     a.seq_slot = _ptr(seq_slot)
     a.n_slots = rows if seq_slot is not None else 0
     a.mode = int(mode)
+    a.len_out, a.lmax_out = _ptr(len_out), _ptr(lmax_out)
     return _keep(a, kv_main, kv_branch, tokens_main, tree_tokens, lens, lmax, pos_ids, path, accept_len, status,
-                 commit_status, seq_slot)
+                 commit_status, seq_slot, len_out, lmax_out)
 
 
 def svt_commit(args: CommitArgs, flags: int = 0, stream=None) -> int:
