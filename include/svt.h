@@ -111,8 +111,8 @@ int svt_build_mask(const int32_t* parents, int32_t B, int32_t M, uint64_t* mask,
 /*   status or SVT_ERR_LENGTH.                                                 */
 /* Arguments: mask [B][T][W] from svt_build_mask; status [B] or NULL; len [B] */
 /* device; lmax host (prefix columns, >= 0); out [B][1][T][lmax + T] of the   */
-/* kind's element (4, 2 or 1 bytes).  Returns SVT_OK, SVT_ERR_ARG /           */
-/* SVT_ERR_UNSUPPORTED (host) or SVT_ERR_HIP.                                 */
+/* kind's element (4, 2 or 1 bytes), 16-byte aligned.  Returns SVT_OK,        */
+/* SVT_ERR_ARG / SVT_ERR_UNSUPPORTED (host) or SVT_ERR_HIP.                   */
 /* ------------------------------------------------------------------------ */
 typedef enum svt_mask_kind { SVT_MASK_ADD_FP32 = 0, SVT_MASK_ADD_BF16 = 1, SVT_MASK_BOOL = 2 } svt_mask_kind;
 

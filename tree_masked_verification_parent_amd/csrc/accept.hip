@@ -55,15 +55,24 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   int bidx = -1;
   if (vec4) {
     // lo is a multiple of 4 (chunk is), the row start is 16-byte aligned.
+    // Four loads in flight per thread before the compares; each thread still
+    // visits its indices in increasing order, so ties keep the lowest index.
     const float4* x4 = reinterpret_cast<const float4*>(x + lo);
     const int n4 = (hi - lo) >> 2;
-    for (int k = tid; k < n4; k += 256) {
-      const float4 v = x4[k];
-      const int i0 = lo + 4 * k;
-      if (bidx < 0 || beats(v.x, best)) { best = v.x; bidx = i0; }
-      if (beats(v.y, best)) { best = v.y; bidx = i0 + 1; }
-      if (beats(v.z, best)) { best = v.z; bidx = i0 + 2; }
-      if (beats(v.w, best)) { best = v.w; bidx = i0 + 3; }
+    for (int k = tid; k < n4; k += 4 * 256) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k + 256 * u < n4) v[u] = x4[k + 256 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (k + 256 * u >= n4) break;
+        const int i0 = lo + 4 * (k + 256 * u);
+        if (bidx < 0 || beats(v[u].x, best)) { best = v[u].x; bidx = i0; }
+        if (beats(v[u].y, best)) { best = v[u].y; bidx = i0 + 1; }
+        if (beats(v[u].z, best)) { best = v[u].z; bidx = i0 + 2; }
+        if (beats(v[u].w, best)) { best = v[u].w; bidx = i0 + 3; }
+      }
     }
     for (int i = lo + 4 * n4 + tid; i < hi; i += 256) {
       const float v = x[i];

@@ -51,9 +51,10 @@ int svt_expand_mask(const uint64_t* mask, const int32_t* status, const int32_t* 
   if (B < 0 || M < 0 || lmax < 0 || kind < SVT_MASK_ADD_FP32 || kind > SVT_MASK_BOOL)
     return finish("svt_expand_mask", SVT_ERR_ARG, shape);
   if (M >= SVT_MAX_T) return finish("svt_expand_mask", SVT_ERR_UNSUPPORTED, shape);
-  if ((int64_t)B * (M + 1) > 65535) return finish("svt_expand_mask", SVT_ERR_UNSUPPORTED, shape);
   if (B == 0) return finish("svt_expand_mask", SVT_OK, shape);
-  if (!mask || !len || !out || !aligned(mask, 8)) return finish("svt_expand_mask", SVT_ERR_ARG, shape);
+  if (!mask || !len || !out || !aligned(mask, 8) || !aligned(out, 16)) return finish("svt_expand_mask", SVT_ERR_ARG, shape);
+  if ((int64_t)B * (M + 1) >= 0x7FFFFFFF || (int64_t)lmax + M + 1 > (int64_t)65535 * 256)
+    return finish("svt_expand_mask", SVT_ERR_UNSUPPORTED, shape);
   return finish("svt_expand_mask", hip_rc(svt::launch_expand_mask(mask, status, len, B, M, lmax, out, kind,
                                                                    seq_status, stream)), shape);
 }

@@ -978,6 +978,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
       row_node[qt] = ok ? r % a.T : -1;
       row_head[qt] = ok ? g * a.G + r / a.T : 0;
       const uint16_t* qrow = q + (((int64_t)cur.b * a.T + (ok ? row_node[qt] : 0)) * a.Hq + row_head[qt]) * D;
+      // the row's mask words and its Q fragments are loaded together and
+      // waited for once
+      const uint64_t* mr = a.mask + ((int64_t)cur.b * a.T + (ok ? row_node[qt] : 0)) * a.W;
+      uint64_t mw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mw[w] = (ok && w < a.W) ? mr[w] : 0ull;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (ok) {
@@ -986,12 +992,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) qf[qt][ks][e] = (__bf16)0.0f;
         }
-        settle(qf[qt][ks]);
       }
-      if (live) {
-        const uint64_t* mr = a.mask + ((int64_t)cur.b * a.T + (ok ? row_node[qt] : 0)) * a.W;
-        for (int w = 0; w < a.W; ++w) s_mask[lt * 16 + n16][w] = ok ? mr[w] : 0ull;
-      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) settle(qf[qt][ks]);
+      if (live)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          if (w < a.W) s_mask[lt * 16 + n16][w] = mw[w];
       m_ref[qt] = row_node[qt] >= 0 ? kNegInf : 0.0f;
       lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
