@@ -1055,10 +1055,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
 }
 
 // Merges the partials of the units that range ends cut, in stream order.
-// Grid (unit, group of 8 rows); 32 threads per row, four dims each.  Units
-// inside a single range return at once.
+// Grid (unit, group of 16 rows); 16 threads per row, eight dims each.  One
+// thread lists the unit's pieces (their partial slots, empty ranges skipped)
+// in LDS; units inside a single range return at once.
+constexpr int kMaxPieces = 64;  // pieces merged per pass of the list
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
+  constexpr int DPT = D / 16;  // dims per thread
   const int u = blockIdx.x;
   const int qb = u % a.nqb, bg = u / a.nqb;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
@@ -1072,36 +1076,62 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   const int64_t E = P + ntl;
   const int c0 = stream_range_of(P, N, G), c1 = stream_range_of(E - 1, N, G);
   if (c0 == c1) return;
-  const int rl = blockIdx.y * 8 + (threadIdx.x >> 5);
-  const int d4 = (threadIdx.x & 31) * 4;
+  __shared__ int s_slot[kMaxPieces];
+  __shared__ int s_np;
+  const int rl = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int d0 = (threadIdx.x & 15) * DPT;
   const int r = qb * a.qb_rows + rl;
-  if (rl >= a.qb_rows || r >= a.R || d4 >= D) return;
+  const bool row_ok = rl < a.qb_rows && r < a.R;
   // Online merge in range order (deterministic); ranges between c0 and c1
   // may be empty (fewer tiles than workgroups) and hold no piece.
   float mx = kNegInf, l = 0.0f;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int cc = c0; cc <= c1; ++cc) {
-    const int64_t hi_c = stream_lo(cc + 1, N, G);
-    if (stream_lo(cc, N, G) == hi_c) continue;
-    const int slot = 2 * cc + ((cc < c1 || E == hi_c) ? 1 : 0);
-    const int64_t pr = (int64_t)slot * a.qb_rows + rl;
-    const float mi = a.ws_ml[pr * 2], li = a.ws_ml[pr * 2 + 1];
-    const f32x4 oi = *reinterpret_cast<const f32x4*>(a.ws_o + pr * D + d4);
-    if (mi == kNegInf) continue;  // no key of this piece is visible to the row
-    const float mn = fmaxf(mx, mi);
-    const float s0 = exp2f(mx - mn), s1 = exp2f(mi - mn);
-    l = l * s0 + li * s1;
-    acc = acc * s0 + oi * s1;
-    mx = mn;
+  float acc[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) acc[e] = 0.0f;
+  for (int cs = c0; cs <= c1; cs += kMaxPieces) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int np = 0;
+      for (int cc = cs; cc <= c1 && cc < cs + kMaxPieces; ++cc) {
+        const int64_t hi_c = stream_lo(cc + 1, N, G);
+        if (stream_lo(cc, N, G) == hi_c) continue;
+        s_slot[np++] = 2 * cc + ((cc < c1 || E == hi_c) ? 1 : 0);
+      }
+      s_np = np;
+    }
+    __syncthreads();
+    if (!row_ok) continue;
+    const int np = s_np;
+#pragma unroll 2
+    for (int k = 0; k < np; ++k) {
+      const int64_t pr = (int64_t)s_slot[k] * a.qb_rows + rl;
+      const float mi = a.ws_ml[pr * 2], li = a.ws_ml[pr * 2 + 1];
+      float oi[DPT];
+#pragma unroll
+      for (int e = 0; e < DPT; e += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_o + pr * D + d0 + e);
+        oi[e] = v[0]; oi[e + 1] = v[1]; oi[e + 2] = v[2]; oi[e + 3] = v[3];
+      }
+      if (mi == kNegInf) continue;  // no key of this piece is visible to the row
+      const float mn = fmaxf(mx, mi);
+      const float s0 = exp2f(mx - mn), s1 = exp2f(mi - mn);
+      l = l * s0 + li * s1;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) acc[e] = acc[e] * s0 + oi[e] * s1;
+      mx = mn;
+    }
   }
+  if (!row_ok) return;
   const float inv = 1.0f / l;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[e] * inv);
   __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
-  *reinterpret_cast<bf16x4*>(orow + d4) = v;
+#pragma unroll
+  for (int e = 0; e < DPT; e += 4) {
+    bf16x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (__bf16)(acc[e + k] * inv);
+    *reinterpret_cast<bf16x4*>(orow + d0 + e) = v;
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -1414,7 +1444,7 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     if (e != hipSuccess) return e;
     const int64_t nu = (int64_t)a->B * a->Hkv * p.nqb;
     if (nu > 0x7FFFFFF0) return hipErrorInvalidValue;
-    const dim3 cg((unsigned)nu, (unsigned)((p.qb_rows + 7) / 8));
+    const dim3 cg((unsigned)nu, (unsigned)((p.qb_rows + 15) / 16));
     if (a->D == 128) hipLaunchKernelGGL((attn_stream_combine_kernel<128>), cg, dim3(256), 0, s, d);
     else hipLaunchKernelGGL((attn_stream_combine_kernel<64>), cg, dim3(256), 0, s, d);
     return hipGetLastError();
