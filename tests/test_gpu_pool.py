@@ -301,3 +301,55 @@ def test_exspec_rounds_match_oracle():
         assert np.array_equal(gtm[s, a:e], tm[s, a:e]), f"tokens slot {s}"
         if a or e != lens0[s]:   # rows that some call wrote position ids for
             assert np.array_equal(gpos[s, :e], opos[s, :e]), f"pos slot {s}"
+
+
+def test_pool_calls_degenerate_shapes():
+    """Empty batches, zero-length contents and a single-node tree."""
+    D, Hkv, L, cap = 64, 1, 1, 32
+    km, tm = _pool(3, Hkv, L, D, cap, 2, 23)
+    # realign of an empty batch: nothing moves, the common end is 0
+    km_t = _dev_rows(km, D, 2)
+    lm = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    rst = torch.full((1,), 77, dtype=torch.int32, device=DEV)
+    e32 = torch.zeros(0, dtype=torch.int32, device=DEV)
+    args = svt.realign_args(km_t[:, :, :0], e32, e32, lm, rst)
+    assert svt.svt_realign(args, svt.SVT_SYNC_CHECK) == 0
+    assert int(H.from_dev(lm)[0]) == 0 and int(H.from_dev(rst)[0]) == 0
+    # realign where every content is empty: ends move, no bytes do
+    rc, gkm, gtm, glm, gpos, grs = _run_realign(km, tm, np.array([0, 0], np.int32), np.array([5, 9], np.int32), D, 2,
+                                                np.array([2, 0], np.int32))
+    assert rc == 0 and grs == 0 and glm == 9 and np.array_equal(gkm, km) and np.array_equal(gtm, tm)
+    assert (gpos[[0, 2], :9] == 0).all()
+    # append commit with M = 0 (a tree of the root alone) on zero-length contents
+    M = 0
+    kb = gen.commit_pattern_bits(np.arange(2 * 2).reshape(1, 2, 2, 1, 1, 1) + 777,
+                                 np.arange(1).reshape(1, 1, 1, 1, 1, 1), np.arange(D).reshape(1, 1, 1, 1, 1, D))
+    tok = np.array([[5], [6]], np.int32)
+    lens = np.array([0, 0], np.int32)
+    al = np.zeros(2, np.int32)
+    path = np.zeros((2, 1), np.int32)
+    slot = np.array([1, 2], np.int32)
+    rc, gkm, gtm, gln, glm, gpos, gcst = _run_commit(km, kb, tm, tok, lens, 0, path, al, D, 2, svt.SVT_COMMIT_APPEND,
+                                                     slot)
+    orc, okm, otm, oln, olm, opos = oracle.commit(km, kb, M, tm, tok, lens, 0, path, al, mode=1, slot=slot)
+    assert rc == 0 and gcst == orc == 0 and gln.tolist() == oln.tolist() == [1, 1] and glm == olm == 1
+    for b, r in enumerate(slot):
+        assert np.array_equal(gkm[:, :, r, :, :1], okm[:, :, r, :, :1]) and gtm[r, 0] == otm[r, 0] == tok[b, 0]
+        assert gpos[r, 0] == 0
+
+
+def test_commit_empty_batch_is_a_no_op():
+    """B = 0: nothing moves; re-pad leaves lmax 0, append keeps it (as the oracle)."""
+    D = 64
+    km = torch.zeros(1, 2, 0, 1, 8, D, dtype=torch.bfloat16, device=DEV)
+    kb = torch.zeros(1, 2, 0, 1, 3, D, dtype=torch.bfloat16, device=DEV)
+    e32 = torch.zeros(0, dtype=torch.int32, device=DEV)
+    for mode in (svt.SVT_COMMIT_REPAD, svt.SVT_COMMIT_APPEND):
+        lm = _i32([4])
+        cst = torch.full((1,), 77, dtype=torch.int32, device=DEV)
+        args = svt.commit_args(km, kb, e32, lm, torch.zeros(0, 3, dtype=torch.int32, device=DEV), e32, cst, mode=mode)
+        assert svt.svt_commit(args, svt.SVT_SYNC_CHECK) == 0
+        orc, _, _, _, olm, _ = oracle.commit(np.zeros((1, 2, 0, 1, 8, D), np.uint16), np.zeros((1, 2, 0, 1, 3, D), np.uint16),
+                                             2, None, np.zeros((0, 3), np.int32), [], 4, np.zeros((0, 3), np.int32),
+                                             np.zeros(0, np.int32), mode=mode)
+        assert int(H.from_dev(cst)[0]) == orc == 0 and int(H.from_dev(lm)[0]) == olm

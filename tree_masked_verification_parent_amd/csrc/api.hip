@@ -132,7 +132,8 @@ static int commit_impl(const char* name, const svt_commit_args* a, bool by_lengt
     return finish(name, SVT_ERR_UNSUPPORTED, shape);
   const int esize = a->dtype == SVT_FP32 ? 4 : 2;
   if ((a->D * esize) % 16 != 0) return finish(name, SVT_ERR_UNSUPPORTED, shape);
-  if (!a->len || !a->lmax || (!by_length && !a->path) || !a->accept_len || !a->commit_status)
+  // per-sequence arrays may be NULL only for an empty batch
+  if (!a->lmax || !a->commit_status || (a->B > 0 && (!a->len || (!by_length && !a->path) || !a->accept_len)))
     return finish(name, SVT_ERR_ARG, shape);
   const bool has_kv = a->n_layers > 0 && a->Hkv > 0 && a->B > 0;
   if (has_kv && (!a->kv_main || !a->kv_branch || !aligned(a->kv_main, 16) || !aligned(a->kv_branch, 16)))
@@ -161,7 +162,7 @@ int svt_realign(const svt_realign_args* a, int32_t flags, hipStream_t stream) {
   if (a->dtype != SVT_FP32 && a->dtype != SVT_BF16) return finish("svt_realign", SVT_ERR_UNSUPPORTED, shape);
   const int esize = a->dtype == SVT_FP32 ? 4 : 2;
   if ((a->D * esize) % 16 != 0) return finish("svt_realign", SVT_ERR_UNSUPPORTED, shape);
-  if (!a->len || !a->end || !a->lmax || !a->realign_status || (a->seq_slot && a->n_slots <= 0))
+  if (!a->lmax || !a->realign_status || (a->B > 0 && (!a->len || !a->end)) || (a->seq_slot && a->n_slots <= 0))
     return finish("svt_realign", SVT_ERR_ARG, shape);
   const bool has_kv = a->n_layers > 0 && a->Hkv > 0 && a->B > 0;
   if (has_kv && (!a->kv_main || !aligned(a->kv_main, 16))) return finish("svt_realign", SVT_ERR_ARG, shape);
