@@ -1055,14 +1055,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
 }
 
 // Merges the partials of the units that range ends cut, in stream order.
-// Grid (unit, group of 16 rows); 16 threads per row, eight dims each.  One
-// thread lists the unit's pieces (their partial slots, empty ranges skipped)
-// in LDS; units inside a single range return at once.
-constexpr int kMaxPieces = 64;  // pieces merged per pass of the list
+// Grid (unit, group of rows): D / DPT threads per row, DPT dims each (the
+// launch picks DPT so that the grid covers the chip).  One thread lists the
+// unit's pieces (their partial slots, empty ranges skipped) in LDS; the
+// partials of four pieces are loaded before they are merged.  Units inside a
+// single range return at once.
+constexpr int kMaxPieces = 64;  // pieces listed per pass
 
-template <int D>
+template <int D, int DPT>
 __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
-  constexpr int DPT = D / 16;  // dims per thread
+  constexpr int TPR = D / DPT;   // threads per row
+  constexpr int RPW = 256 / TPR; // rows per workgroup
+  constexpr int KB = 4;          // pieces loaded per batch
   const int u = blockIdx.x;
   const int qb = u % a.nqb, bg = u / a.nqb;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
@@ -1078,8 +1082,8 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   if (c0 == c1) return;
   __shared__ int s_slot[kMaxPieces];
   __shared__ int s_np;
-  const int rl = blockIdx.y * 16 + (threadIdx.x >> 4);
-  const int d0 = (threadIdx.x & 15) * DPT;
+  const int rl = blockIdx.y * RPW + threadIdx.x / TPR;
+  const int d0 = (threadIdx.x % TPR) * DPT;
   const int r = qb * a.qb_rows + rl;
   const bool row_ok = rl < a.qb_rows && r < a.R;
   // Online merge in range order (deterministic); ranges between c0 and c1
@@ -1102,35 +1106,54 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
     __syncthreads();
     if (!row_ok) continue;
     const int np = s_np;
-#pragma unroll 2
-    for (int k = 0; k < np; ++k) {
-      const int64_t pr = (int64_t)s_slot[k] * a.qb_rows + rl;
-      const float mi = a.ws_ml[pr * 2], li = a.ws_ml[pr * 2 + 1];
-      float oi[DPT];
+    for (int k = 0; k < np; k += KB) {
+      float mi[KB], li[KB], oi[KB][DPT];
 #pragma unroll
-      for (int e = 0; e < DPT; e += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_o + pr * D + d0 + e);
-        oi[e] = v[0]; oi[e + 1] = v[1]; oi[e + 2] = v[2]; oi[e + 3] = v[3];
+      for (int j = 0; j < KB; ++j) {
+        if (k + j >= np) break;
+        const int64_t pr = (int64_t)s_slot[k + j] * a.qb_rows + rl;
+        mi[j] = a.ws_ml[pr * 2];
+        li[j] = a.ws_ml[pr * 2 + 1];
+        const float* src = a.ws_o + pr * D + d0;
+        if constexpr (DPT % 4 == 0) {
+#pragma unroll
+          for (int e = 0; e < DPT; e += 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
+            oi[j][e] = v[0]; oi[j][e + 1] = v[1]; oi[j][e + 2] = v[2]; oi[j][e + 3] = v[3];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < DPT; ++e) oi[j][e] = src[e];
+        }
       }
-      if (mi == kNegInf) continue;  // no key of this piece is visible to the row
-      const float mn = fmaxf(mx, mi);
-      const float s0 = exp2f(mx - mn), s1 = exp2f(mi - mn);
-      l = l * s0 + li * s1;
 #pragma unroll
-      for (int e = 0; e < DPT; ++e) acc[e] = acc[e] * s0 + oi[e] * s1;
-      mx = mn;
+      for (int j = 0; j < KB; ++j) {
+        if (k + j >= np) break;
+        if (mi[j] == kNegInf) continue;  // no key of this piece is visible to the row
+        const float mn = fmaxf(mx, mi[j]);
+        const float s0 = exp2f(mx - mn), s1 = exp2f(mi[j] - mn);
+        l = l * s0 + li[j] * s1;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) acc[e] = acc[e] * s0 + oi[j][e] * s1;
+        mx = mn;
+      }
     }
   }
   if (!row_ok) return;
   const float inv = 1.0f / l;
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
+  if constexpr (DPT % 4 == 0) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int e = 0; e < DPT; e += 4) {
-    bf16x4 v;
+    for (int e = 0; e < DPT; e += 4) {
+      bf16x4 v;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = (__bf16)(acc[e + k] * inv);
-    *reinterpret_cast<bf16x4*>(orow + d0 + e) = v;
+      for (int k = 0; k < 4; ++k) v[k] = (__bf16)(acc[e + k] * inv);
+      *reinterpret_cast<bf16x4*>(orow + d0 + e) = v;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) orow[d0 + e] = (__bf16)(acc[e] * inv);
   }
 }
 
@@ -1444,9 +1467,18 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     if (e != hipSuccess) return e;
     const int64_t nu = (int64_t)a->B * a->Hkv * p.nqb;
     if (nu > 0x7FFFFFF0) return hipErrorInvalidValue;
-    const dim3 cg((unsigned)nu, (unsigned)((p.qb_rows + 15) / 16));
-    if (a->D == 128) hipLaunchKernelGGL((attn_stream_combine_kernel<128>), cg, dim3(256), 0, s, d);
-    else hipLaunchKernelGGL((attn_stream_combine_kernel<64>), cg, dim3(256), 0, s, d);
+    // dims per thread: the largest of 8, 4, 2 that still gives two workgroups per CU
+    const int want = 2 * p.grid;
+    const int dpt = (nu * ((p.qb_rows + 256 / (a->D / 8) - 1) / (256 / (a->D / 8))) >= want) ? 8
+                    : (nu * ((p.qb_rows + 256 / (a->D / 4) - 1) / (256 / (a->D / 4))) >= want) ? 4 : 2;
+    const int rpw = 256 / (a->D / dpt);
+    const dim3 cg((unsigned)nu, (unsigned)((p.qb_rows + rpw - 1) / rpw));
+#define SVT_COMBINE(DD)                                                                                   \
+  if (dpt == 8) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 8>), cg, dim3(256), 0, s, d);          \
+  else if (dpt == 4) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 4>), cg, dim3(256), 0, s, d);     \
+  else hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 2>), cg, dim3(256), 0, s, d);
+    if (a->D == 128) { SVT_COMBINE(128) } else { SVT_COMBINE(64) }
+#undef SVT_COMBINE
     return hipGetLastError();
   }
   const int64_t nunits = (int64_t)a->B * a->Hkv * p.ns;
