@@ -593,12 +593,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 // --------------------------------------------------------------------------
 // bf16 MFMA kernel, stream form (used when a KV head has three or more query
 // tiles).  A work unit is one (sequence, KV head, query block): up to 12
-// query tiles of 16 rows, one per wave, so every K/V tile of the unit crosses
-// HBM -> LDS once and feeds all of its query rows.  A unit's key tiles are its
-// prefix tiles followed by its tree tiles; the tiles of all units, concatenated
-// in unit order, form one stream that is cut into gridDim.x equal ranges, one
-// per workgroup (one workgroup per CU).  A workgroup walks its range with one
-// 4-deep DMA ring that runs across unit boundaries.  A unit lying wholly inside
+// query tiles of 16 rows, one per compute wave, so every K/V tile of the unit
+// crosses HBM -> LDS once and feeds all of its query rows.  A unit's key tiles
+// are its prefix tiles followed by its tree tiles; the tiles of all units,
+// concatenated in unit order, form one stream that is cut into gridDim.x equal
+// ranges, one per workgroup (one workgroup per CU).  A workgroup walks its
+// range with one 4-deep DMA ring that runs across unit boundaries, fed by two
+// producer waves (one copies the K planes, the other the V planes) that do no
+// arithmetic: copies that stall on issue under memory back-pressure never hold
+// up a compute wave, and the compute waves' own loads (Q, mask words) never
+// wait behind tile copies.  A unit lying wholly inside
 // one range is normalised and written directly; a unit cut by range ends
 // leaves (m, l, O) partials in two slots per workgroup (slot 2c: a piece that
 // ends at its unit's end, slot 2c+1: the piece that ends at the range end), and
@@ -620,18 +624,21 @@ __device__ __forceinline__ int64_t stream_lo(int64_t c, int64_t n, int g) { retu
 // Range holding stream tile x.
 __device__ __forceinline__ int stream_range_of(int64_t x, int64_t n, int g) { return (int)(((x + 1) * g - 1) / n); }
 
+// NW compute waves (QMAX query tiles each) and two producer waves.
 template <int D, int NW, int QMAX>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
+__global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev a) {
+  constexpr int NP = 2;  // producer waves: K planes, V planes
   constexpr int kStages = 4;
   constexpr int NKS = D / 32;
   constexpr int NDT = D / 16;
-  constexpr int NT = NW * 64;
+  constexpr int NT = (NW + NP) * 64;
   using TL = Tile<D, NW>;
+  static_assert(3 * TL::NINSTR < 64, "a producer's three tiles in flight must fit its vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * TL::STAGEB];
   __shared__ int s_pref[kStreamMaxB + 1];  // s_pref[b] = tiles of sequences < b (per unit)
   __shared__ int s_len[kStreamMaxB];
   __shared__ int s_row[kStreamMaxB];  // cache row of each sequence
-  __shared__ int s_wsum[NW];
+  __shared__ int s_wsum[NW + NP];
   __shared__ int s_carry;
   __shared__ uint64_t s_mask[NW * QMAX * 16][4];  // each lane's tree-mask words, its own rows only
 
@@ -753,42 +760,23 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
       tree_t = t - r.np;
     }
   };
-  // Lane-constant element offsets of this wave's copies for a full tile.
-  int cofk[TL::PER_WAVE], cofv[TL::PER_WAVE];
-#pragma unroll
-  for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
-    const int ins = (wave + NW * jj) % TL::NINSTR;
-    const int row = ins * TL::RPI + lane / TL::CPR;
-    const int slot = lane % TL::CPR;
-    cofk[jj] = row * D + 8 * (slot ^ TL::swz_k(row));
-    cofv[jj] = row * D + 8 * (slot ^ TL::swz_v(row));
-  }
+  // Producer wave p (wave NW + p) copies plane p (0: K, 1: V) of every tile,
+  // NINSTR 1 KB copies per tile.  Rows past the valid ones of a partial tile
+  // repeat its last valid row; they are masked.
+  const int pw = wave - NW;
   auto issue_tile = [&](const Cur& r, int64_t x, int st) {
     const uint16_t *kb, *vb;
     int nvalid, tree_t;
     tile_src(r, x, kb, vb, nvalid, tree_t);
-    unsigned char* kl = lds + st * TL::STAGEB;
-    unsigned char* vl = kl + TL::TILEB;
-    if (nvalid == KT) {
+    const uint16_t* src = pw == 0 ? kb : vb;
+    unsigned char* dst = lds + st * TL::STAGEB + (pw == 0 ? 0 : TL::TILEB);
 #pragma unroll
-      for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
-        if (!TL::has_copy(wave, jj)) continue;
-        const int ins = (wave + NW * jj) % TL::NINSTR;
-        copy16_to_lds(kb + cofk[jj], kl + ins * 1024);
-        copy16_to_lds(vb + cofv[jj], vl + ins * 1024);
-      }
-    } else {
-      // Rows past the valid ones repeat the last valid row; they are masked.
-#pragma unroll
-      for (int jj = 0; jj < TL::PER_WAVE; ++jj) {
-        if (!TL::has_copy(wave, jj)) continue;
-        const int ins = (wave + NW * jj) % TL::NINSTR;
-        const int row = ins * TL::RPI + lane / TL::CPR;
-        const int slot = lane % TL::CPR;
-        const int src = min(row, nvalid - 1) * D;
-        copy16_to_lds(kb + src + 8 * (slot ^ TL::swz_k(row)), kl + ins * 1024);
-        copy16_to_lds(vb + src + 8 * (slot ^ TL::swz_v(row)), vl + ins * 1024);
-      }
+    for (int ins = 0; ins < TL::NINSTR; ++ins) {
+      const int row = ins * TL::RPI + lane / TL::CPR;
+      const int slot = lane % TL::CPR;
+      const int sw = pw == 0 ? TL::swz_k(row) : TL::swz_v(row);
+      const int srow = nvalid == KT ? row : min(row, nvalid - 1);
+      copy16_to_lds(src + srow * D + 8 * (slot ^ sw), dst + ins * 1024);
     }
   };
 
@@ -818,26 +806,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     cur = locate(lo);
     pcur = cur;
   }
-  // Producer: a cursor that issues the copies of stream tile y + 2 once tile
-  // y is visible.  landed(y): wait until tile y's copies are done (only tile
-  // y + 1 may still be in flight), barrier, then issue tile y + 2 into the
-  // stage that tile y - 2 used (every wave has finished with it: its P V ran
-  // before this barrier).  While a wave works on tiles y - 1 (P V) and y
-  // (scores), tiles y + 1 and y + 2 are in flight: four stages.
+  // Producer cursor: pcur/px walk the range ahead of the compute waves.
   int64_t px = lo;
   auto produce = [&](int st) {
     if (px == pcur.base + pcur.ntl) advance(pcur);
     issue_tile(pcur, px, st);
     ++px;
   };
-  if (lo < hi) produce(0);
-  if (lo + 1 < hi) produce(1);
-  auto landed = [&](int64_t y) {
-    if (y + 1 < hi) TL::template wait_tiles<1>(wave);
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (y + 2 < hi) produce((int)((y - lo + 2) % kStages));
-  };
+  // Tile y is visible to the compute waves after barrier y (one barrier per
+  // tile for every wave of the workgroup; the producers pass it once their
+  // copies of tile y are done).
+  auto landed = [&](int64_t) { lds_barrier(); };
 
   // Scores of stream tile y for NQ query tiles: s[qt][u][e] = score of key
   // 16u + 4*grp + e of the tile for query n16.
@@ -927,40 +906,42 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_stream_kernel(AttnDev a) {
     }
   };
 
-  // The tiles of one piece for a wave with NQ live query tiles, software
-  // pipelined: the scores of tile x + 1 are issued before the softmax and
-  // P V of tile x, so the matrix cores have independent work while the
-  // softmax runs.  Each piece runs one instance, so the accumulators keep
-  // their registers.
+  // The tiles of one piece for a compute wave with NQ live query tiles.  A
+  // wave is done with tile x before it arrives at barrier x + 1, which lets
+  // the producers refill that stage right after the barrier (three tiles in
+  // flight with four stages); the matrix cores overlap the softmax of one
+  // wave with the MFMAs of the others.  Each piece runs one instance, so the
+  // accumulators keep their registers.
   auto run_piece = [&](auto nq_c, int64_t x0, int64_t x1) {
     constexpr int NQ = decltype(nq_c)::value;
     if constexpr (NQ == 0) {
       for (int64_t x = x0; x < x1; ++x) landed(x);
     } else {
-      f32x4 sa[NQ][4], sb[NQ][4];
-      landed(x0);
-      scores(nq_c, x0, sa);
-      int64_t x = x0;
-      while (x + 2 < x1) {
-        landed(x + 1);
-        scores(nq_c, x + 1, sb);
-        finish(nq_c, x, sa);
-        landed(x + 2);
-        scores(nq_c, x + 2, sa);
-        finish(nq_c, x + 1, sb);
-        x += 2;
-      }
-      if (x + 1 < x1) {
-        landed(x + 1);
-        scores(nq_c, x + 1, sb);
-        finish(nq_c, x, sa);
-        finish(nq_c, x + 1, sb);
-      } else {
+      f32x4 sa[NQ][4];
+      for (int64_t x = x0; x < x1; ++x) {
+        landed(x);
+        scores(nq_c, x, sa);
         finish(nq_c, x, sa);
       }
     }
   };
 
+  if (wave >= NW) {
+    // Producer: three tiles ahead.  Before barrier y it waits for its copies
+    // of tile y (tiles y + 1 and y + 2 may still be in flight); after it, it
+    // issues tile y + 3 into the stage of tile y - 1, which every compute
+    // wave finished before arriving at barrier y.
+    if (lo < hi) produce(0);
+    if (lo + 1 < hi) produce(1);
+    if (lo + 2 < hi) produce(2);
+    for (int64_t y = lo; y < hi; ++y) {
+      if (y + 2 < hi) wait_vmcnt<2 * TL::NINSTR>();
+      else if (y + 1 < hi) wait_vmcnt<TL::NINSTR>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (y + 3 < hi) produce((int)((y - lo + 3) % kStages));
+    }
+  } else
   for (int64_t x = lo; x < hi;) {
     // ---- a piece of unit `cur`: [x, pend)
     const int64_t pend = min(hi, cur.base + (int64_t)cur.ntl);
@@ -1363,8 +1344,8 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->qb_rows = (p->nw / p->nwk) * p->qw * 16;
   } else if (a->dtype == SVT_BF16) {
     // Stream form: up to 12 query tiles per unit, spread evenly over the
-    // fewest units per KV head, two tiles per wave (each K or V fragment read
-    // from LDS feeds two MFMAs); one workgroup per CU.
+    // fewest units per KV head, one tile per compute wave (plus the two
+    // producer waves); one workgroup per CU.
     const int nqb = (p->nqt + 11) / 12;
     const int tpb = (p->nqt + nqb - 1) / nqb;
     p->wide = 1;
@@ -1455,11 +1436,11 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   if (p.wide) {
     const dim3 g(p.grid);
 #define SVT_STREAM(DD)                                                                                 \
-  switch (p.nw) {                                                                                      \
-    case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4, 1>), g, dim3(256), 0, s, d); break;       \
-    case 6: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6, 1>), g, dim3(384), 0, s, d); break;       \
-    case 9: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 9, 1>), g, dim3(576), 0, s, d); break;       \
-    default: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 12, 1>), g, dim3(768), 0, s, d); break;     \
+  switch (p.nw) { /* compute waves; two producer waves on top */                                       \
+    case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4, 1>), g, dim3(6 * 64), 0, s, d); break;    \
+    case 6: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6, 1>), g, dim3(8 * 64), 0, s, d); break;    \
+    case 9: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 9, 1>), g, dim3(11 * 64), 0, s, d); break;   \
+    default: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 12, 1>), g, dim3(14 * 64), 0, s, d); break; \
   }
     if (a->D == 128) { SVT_STREAM(128) } else { SVT_STREAM(64) }
 #undef SVT_STREAM
