@@ -619,10 +619,20 @@ __device__ __forceinline__ int stream_seq_tiles(const AttnDev& a, int b, int lma
   return *code == SVT_OK ? (L + KT - 1) / KT + (a.T + KT - 1) / KT : 0;
 }
 
+// floor(a / b) for 0 <= a < 2^53 and 0 < b < 2^53: the double quotient is
+// within one of it (relative error below 2^-53), one integer step corrects
+// it.  Cheaper than the 64-bit integer division, which is a long software
+// sequence on the GPU.
+__device__ __forceinline__ int64_t div_floor(int64_t a, int64_t b) {
+  int64_t q = (int64_t)((double)a / (double)b);
+  if (q * b > a) --q;
+  else if ((q + 1) * b <= a) ++q;
+  return q;
+}
 // Stream position of the first tile of workgroup range c (ranges are floor(c*N/G)).
-__device__ __forceinline__ int64_t stream_lo(int64_t c, int64_t n, int g) { return c * n / g; }
+__device__ __forceinline__ int64_t stream_lo(int64_t c, int64_t n, int g) { return div_floor(c * n, g); }
 // Range holding stream tile x.
-__device__ __forceinline__ int stream_range_of(int64_t x, int64_t n, int g) { return (int)(((x + 1) * g - 1) / n); }
+__device__ __forceinline__ int stream_range_of(int64_t x, int64_t n, int g) { return (int)div_floor((x + 1) * g - 1, n); }
 
 // NW compute waves (QMAX query tiles each) and two producer waves.
 template <int D, int NW, int QMAX>
@@ -1037,17 +1047,17 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
 
 // Merges the partials of the units that range ends cut, in stream order.
 // Grid (unit, group of rows): D / DPT threads per row, DPT dims each (the
-// launch picks DPT so that the grid covers the chip).  One thread lists the
-// unit's pieces (their partial slots, empty ranges skipped) in LDS; the
-// partials of four pieces are loaded before they are merged.  Units inside a
-// single range return at once.
-constexpr int kMaxPieces = 64;  // pieces listed per pass
+// launch picks DPT so that the grid covers the chip).  The first wave lists
+// the unit's pieces (their partial slots, empty ranges skipped) in LDS, one
+// range per lane; the partials of KB pieces are loaded before any of them is
+// merged.  Units inside a single range return at once.
+constexpr int kMaxPieces = 64;  // pieces listed per pass (one wave)
 
 template <int D, int DPT>
 __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   constexpr int TPR = D / DPT;   // threads per row
   constexpr int RPW = 256 / TPR; // rows per workgroup
-  constexpr int KB = 4;          // pieces loaded per batch
+  constexpr int KB = 4;        // pieces loaded per batch
   const int u = blockIdx.x;
   const int qb = u % a.nqb, bg = u / a.nqb;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
@@ -1075,14 +1085,19 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   for (int e = 0; e < DPT; ++e) acc[e] = 0.0f;
   for (int cs = c0; cs <= c1; cs += kMaxPieces) {
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int np = 0;
-      for (int cc = cs; cc <= c1 && cc < cs + kMaxPieces; ++cc) {
+    if (threadIdx.x < kMaxPieces) {
+      const int cc = cs + (int)threadIdx.x;
+      bool has = false;
+      int slot = 0;
+      if (cc <= c1) {
         const int64_t hi_c = stream_lo(cc + 1, N, G);
-        if (stream_lo(cc, N, G) == hi_c) continue;
-        s_slot[np++] = 2 * cc + ((cc < c1 || E == hi_c) ? 1 : 0);
+        has = stream_lo(cc, N, G) != hi_c;
+        slot = 2 * cc + ((cc < c1 || E == hi_c) ? 1 : 0);
       }
-      s_np = np;
+      const uint64_t bal = __ballot(has);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (has) s_slot[below] = slot;
+      if (threadIdx.x == 0) s_np = (int)__popcll(bal);
     }
     __syncthreads();
     if (!row_ok) continue;
