@@ -78,7 +78,7 @@ int svt_verify_attention(const svt_attn_args* a, hipStream_t stream) {
   if (a->M >= SVT_MAX_T || (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
     return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);
   if (a->form == SVT_ATTN_STREAM &&
-      (a->dtype != SVT_BF16 || ((a->Hq / a->Hkv) * (a->M + 1) + 15) / 16 < 3 || a->B > svt::kStreamMaxBatch))
+      (a->dtype != SVT_BF16 || a->B > svt::kStreamMaxBatch))
     return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);
   if (a->B == 0) return finish("svt_verify_attention", SVT_OK, shape);
   if (!a->q || !a->k_cache || !a->v_cache || !a->len || !a->lmax || !a->k_tree || !a->v_tree || !a->mask ||

@@ -591,8 +591,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 }
 
 // --------------------------------------------------------------------------
-// bf16 MFMA kernel, stream form (used when a KV head has three or more query
-// tiles).  A work unit is one (sequence, KV head, query block): up to 12
+// bf16 MFMA kernel, stream form (used when the batch gives every CU eight or
+// more key tiles).  A work unit is one (sequence, KV head, query block): up to 12
 // query tiles of 16 rows, one per compute wave, so every K/V tile of the unit
 // crosses HBM -> LDS once and feeds all of its query rows.  A unit's key tiles
 // are its prefix tiles followed by its tree tiles; the tiles of all units,
@@ -1339,7 +1339,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   const int64_t stream_tiles = (int64_t)a->B * a->Hkv * ((p->nqt + 11) / 12) *
                                (((int64_t)a->lmax_bound + KT - 1) / KT + (p->T + KT - 1) / KT);
   const int cus = a->dtype == SVT_BF16 ? device_cu_count() : 0;
-  const bool stream_ok = p->nqt >= 3 && a->B <= kStreamMaxB;
+  const bool stream_ok = a->B <= kStreamMaxB;
   bool use_stream = stream_ok && stream_tiles >= 8 * (int64_t)cus;
   if (a->form == SVT_ATTN_SPLIT) use_stream = false;
   if (a->form == SVT_ATTN_STREAM) {
@@ -1347,10 +1347,9 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     use_stream = true;
   }
   if (a->dtype == SVT_BF16 && !use_stream) {
-    // One or two query tiles, very many sequences, or a stream too short to
-    // give every CU eight tiles: the split form, four waves per workgroup;
-    // with one or two query tiles two waves share the rows and split every
-    // key tile.
+    // Very many sequences or a stream too short to give every CU eight
+    // tiles: the split form, four waves per workgroup; with one or two query
+    // tiles two waves share the rows and split every key tile.
     p->wide = 0;
     p->nw = 4;
     p->qw = 1;
@@ -1364,7 +1363,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     const int nqb = (p->nqt + 11) / 12;
     const int tpb = (p->nqt + nqb - 1) / nqb;
     p->wide = 1;
-    p->nw = tpb <= 4 ? 4 : tpb <= 6 ? 6 : tpb <= 9 ? 9 : 12;
+    p->nw = tpb <= 2 ? tpb : tpb <= 4 ? 4 : tpb <= 6 ? 6 : tpb <= 9 ? 9 : 12;
     p->qw = 1;
     p->nwk = 1;
     p->stages = 4;
@@ -1452,6 +1451,8 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     const dim3 g(p.grid);
 #define SVT_STREAM(DD)                                                                                 \
   switch (p.nw) { /* compute waves; two producer waves on top */                                       \
+    case 1: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 1, 1>), g, dim3(3 * 64), 0, s, d); break;    \
+    case 2: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 2, 1>), g, dim3(4 * 64), 0, s, d); break;    \
     case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4, 1>), g, dim3(6 * 64), 0, s, d); break;    \
     case 6: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6, 1>), g, dim3(8 * 64), 0, s, d); break;    \
     case 9: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 9, 1>), g, dim3(11 * 64), 0, s, d); break;   \
