@@ -1290,18 +1290,39 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
   const int ns_b = max(1, (L + a.kc - 1) / a.kc);
   if (ns_b <= 1) return;
   const int64_t base = ((int64_t)b * a.Hkv + g) * a.ns;
+  // The loads of KB splits are issued before any of them is used, so a
+  // merge pays few memory round trips; the arithmetic runs in split order.
+  constexpr int KB = 8;
   float mx = kNegInf;
-  for (int s = 0; s < ns_b; ++s) mx = fmaxf(mx, a.ws_ml[((base + s) * a.R + r) * 2]);
+  for (int s0 = 0; s0 < ns_b; s0 += KB) {
+    float mv[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) mv[j] = s0 + j < ns_b ? a.ws_ml[((base + s0 + j) * a.R + r) * 2] : kNegInf;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) mx = fmaxf(mx, mv[j]);
+  }
   const float mu = mx == kNegInf ? 0.0f : mx;
   float lsum = 0.0f, acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  for (int s = 0; s < ns_b; ++s) {
-    const int64_t pr = (base + s) * a.R + r;
-    const float w = exp2f(a.ws_ml[pr * 2] - mu);
-    lsum += a.ws_ml[pr * 2 + 1] * w;
+  for (int s0 = 0; s0 < ns_b; s0 += KB) {
+    float mv[KB], lv[KB], ov[KB][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] += a.ws_o[pr * D + lane + 64 * e] * w;
+    for (int j = 0; j < KB; ++j) {
+      const int64_t pr = (base + min(s0 + j, ns_b - 1)) * a.R + r;
+      mv[j] = a.ws_ml[pr * 2];
+      lv[j] = a.ws_ml[pr * 2 + 1];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ov[j][e] = a.ws_o[pr * D + lane + 64 * e];
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (s0 + j >= ns_b) break;
+      const float w = exp2f(mv[j] - mu);
+      lsum += lv[j] * w;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += ov[j][e] * w;
+    }
   }
   E* orow = static_cast<E*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
   const float inv = 1.0f / lsum;
