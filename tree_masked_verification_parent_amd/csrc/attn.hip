@@ -8,33 +8,31 @@
 // padding of the prefix: Batch Speculative Decoding Done Right (ko summary,
 // section 2, rectangular alignment).
 //
-// Work decomposition (one launch covers the whole batch):
-//   * A KV head g of sequence b serves G = Hq/Hkv query heads, so its query
-//     rows are r = hl*T + i (hl < G, node i < T): R = G*T rows that all read
-//     the same keys.  This is what makes Q K^T and P V dense contractions.
-//   * Rows are cut into 16-row tiles; a workgroup (4 waves) owns a block of
-//     tiles, each wave `qw` of them (or 2 waves share one tile row-set and
-//     split each key tile when there are only 1-2 tiles).
-//   * The prefix is cut into splits of `kc` keys; the last split of a sequence
-//     also takes the tree keys (in 64-key tiles, tile t uses mask word t).
-//     Splits of one sequence write (m, l, O) partials that a second kernel
-//     merges in split order, so results are bitwise reproducible.
-//   * Workgroup ids are remapped so that the query blocks sharing one key
-//     split run on the same XCD (hardware dispatches ids round-robin over the
-//     8 XCDs) and share its L2.
+// The G = Hq/Hkv query heads of a KV head g of sequence b give R = G*T query
+// rows r = hl*T + i (hl < G, node i < T) that all read the same keys, so
+// Q K^T and P V are dense contractions (bf16 MFMA).  Rows are cut into 16-row
+// query tiles.  Two decompositions compute the same function:
+//   * stream form (attn_bf16_stream_kernel + attn_stream_combine_kernel): the
+//     64-key tiles of all (sequence, KV head, query block) units form one
+//     stream cut into one equal range per CU; compute waves own one query tile
+//     each, two producer waves stream K and V tiles HBM -> LDS; units cut by
+//     range ends leave (m, l, O) partials merged in stream order.
+//   * split form (attn_bf16_kernel + attn_combine_kernel): one workgroup per
+//     (sequence, KV head, query block, prefix split of kc keys); the last split
+//     also takes the tree keys; splits are merged in split order.
+// Both are bitwise reproducible for identical inputs.  Tree tile t of a row
+// uses its mask word t; masked keys get probability 0 exactly.
 //
-// bf16 path, per 64-key tile: the workgroup copies K and V rows (coalesced
-// 16-byte loads, prefetched one tile ahead in registers) into LDS, rows
-// padded against bank conflicts.  Each wave computes S^T = K Q^T with
-// v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dims read as one 16-byte LDS
-// word per lane, B = the wave's Q fragment kept in registers), so a lane ends
-// up holding 8 scores of one query row.  Online softmax runs in fp32 in the
-// base-2 domain.  Then O^T += V^T P^T: P (rounded to bf16) is already in the B
-// operand layout, and V^T comes from LDS with ds_read_b64_tr_b16, which hands
-// lane (d, group) the values of 4 keys at dimension d.
+// bf16 math, per 64-key tile: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16
+// keys x 32 dims, one 16-byte LDS read per lane; B = the wave's Q fragment in
+// registers), so a lane holds 16 scores of one query row.  Online softmax in
+// fp32, base 2.  O^T += V^T P^T: P (rounded to bf16) is already in the B
+// operand layout, and V^T comes from LDS with ds_read_b64_tr_b16.  Tiles land
+// in LDS unpadded, XOR-swizzled against bank conflicts, by global_load_lds
+// copies issued as inline assembly (waits are explicit).
 //
-// fp32 path: the same split structure with VALU arithmetic (one lane per key
-// for Q K^T, one lane per dimension for P V).
+// fp32 path: the split structure with VALU arithmetic (one lane per key for
+// Q K^T, one lane per dimension for P V).
 #include <type_traits>
 
 #include "svt_internal.h"
