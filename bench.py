@@ -71,17 +71,18 @@ def sources_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernels):
+def measured_traffic(kernels, workload):
     """HBM bytes per launch of the given kernels from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factors), or
-    None when the summary is missing or the kernel sources changed since."""
+    None when the summary is missing, was taken on another workload, or the
+    kernel sources changed since."""
     import json as _json
     try:
         with open(TRAFFIC_FILE) as f:
             t = _json.load(f)
     except OSError:
         return None
-    if t.get("sources_digest") != sources_digest():
+    if t.get("sources_digest") != sources_digest() or t.get("workload", "").split(" ")[0] != workload:
         return None
     total = 0.0
     for k in kernels:
@@ -695,13 +696,13 @@ def main():
             a = commit_gbps
             return {"kernel": "commit_move_kernel (+ commit_finalize_kernel)", "bound": "hbm", "achieved": a,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
-                    "traffic": measured_traffic(["commit_move_kernel"]),
+                    "traffic": measured_traffic(["commit_move_kernel"], w.name),
                     "bytes_per_launch": commit_bytes, "avg_launch_us": t_commit * 1e6}
         if kind == "attention":
             a = attn_gbps
             return {"kernel": "attn_bf16_stream_kernel (+ attn_stream_combine_kernel)", "bound": "hbm",
                     "achieved": a, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
-                    "traffic": measured_traffic(["attn_bf16_stream_kernel", "attn_stream_combine_kernel"]),
+                    "traffic": measured_traffic(["attn_bf16_stream_kernel", "attn_stream_combine_kernel"], w.name),
                     "bytes_per_launch": attn_bytes, "avg_launch_us": t_attn * 1e6,
                     "mfma_tflops": attn_flops / t_attn / 1e12,
                     "mfma_frac": attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS}
@@ -709,7 +710,7 @@ def main():
             a = acc_bytes / t_accept / 1e9
             return {"kernel": "argmax_partial_kernel (+ accept_kernel)", "bound": "hbm", "achieved": a,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
-                    "traffic": measured_traffic(["argmax_partial_kernel", "accept_kernel"]),
+                    "traffic": measured_traffic(["argmax_partial_kernel", "accept_kernel"], w.name),
                     "bytes_per_launch": acc_bytes, "avg_launch_us": t_accept * 1e6}
         return {"kernel": "build_mask_kernel", "bound": "latency", "achieved": None, "peak": None,
                 "unit": None, "frac": None, "traffic": None, "avg_launch_us": t_mask * 1e6}
