@@ -1154,11 +1154,16 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
 // --------------------------------------------------------------------------
 // fp32 VALU kernel: 64 query rows per workgroup, 16 per wave.
 // --------------------------------------------------------------------------
+// Each wave runs its rows one after another (a chain of dependent LDS reads
+// per row), so few rows per wave and more workgroups keep the latency down.
+constexpr int kFp32RowsPerWave = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
   constexpr int DPL = D / 64;  // dims per lane
   constexpr int KS = D + 1;    // padded K row (floats) against bank conflicts
-  __shared__ float qs[64 * D];
+  constexpr int RPW = kFp32RowsPerWave;  // query rows per wave, handled one after another
+  __shared__ float qs[4 * RPW * D];
   __shared__ float ks[KT * KS];
   __shared__ float vs[KT * D];
   __shared__ float ps[4][KT];
@@ -1177,17 +1182,17 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
   const float* __restrict__ ktr = static_cast<const float*>(a.ktree);
   const float* __restrict__ vtr = static_cast<const float*>(a.vtree);
   const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
-  const int r0 = c.qb * 64;
+  const int r0 = c.qb * 4 * RPW;
 
-  for (int x = tid; x < 64 * D; x += 256) {
+  for (int x = tid; x < 4 * RPW * D; x += 256) {
     const int rr = x / D, d = x % D, r = r0 + rr;
     float v = 0.0f;
     if (r < a.R) v = q[(((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D + d];
     qs[x] = v;
   }
-  float m_run[16], l_run[16], o[16][DPL];
+  float m_run[RPW], l_run[RPW], o[RPW][DPL];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < RPW; ++j) {
     m_run[j] = kNegInf;
     l_run[j] = 0.0f;
 #pragma unroll
@@ -1219,8 +1224,8 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
     }
     __syncthreads();
 #pragma unroll 1
-    for (int j = 0; j < 16; ++j) {
-      const int rr = wave * 16 + j, r = r0 + rr;
+    for (int j = 0; j < RPW; ++j) {
+      const int rr = wave * RPW + j, r = r0 + rr;
       if (r >= a.R) break;  // wave-uniform
       const int node = r % a.T;
       bool ok = lane < nvalid;
@@ -1253,8 +1258,8 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
   }
   const bool direct = c.ns_b == 1;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = r0 + wave * 16 + j;
+  for (int j = 0; j < RPW; ++j) {
+    const int r = r0 + wave * RPW + j;
     if (r >= a.R) break;
     if (direct) {
       float* orow = static_cast<float*>(a.out) + (((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D;
@@ -1396,7 +1401,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->qw = 1;
     p->nw = 4;
     p->stages = 1;
-    p->qb_rows = 64;
+    p->qb_rows = 4 * kFp32RowsPerWave;
   }
   p->nqb = (p->R + p->qb_rows - 1) / p->qb_rows;
   if (p->wide) {
