@@ -378,6 +378,31 @@ def test_attention_parity(name, over, lens, form):
     H.check_attention(w, H.out_f32(w, out), ref, name)
 
 
+MANY_CASES = [
+    # more sequences than the stream form's workgroup has threads (its per-sequence
+    # prefix scan runs in several passes), one query tile per KV head
+    ("b300-decode-1wave", dict(B=300, dtype="bf16", Hq=2, Hkv=2, D=64, M=0), 150),
+    ("b1024-M3-1wave", dict(B=1024, dtype="bf16", Hq=1, Hkv=1, D=64, M=3), 80),
+]
+
+
+@pytest.mark.parametrize("form", FORMS[1:], ids=FORM_IDS[1:])
+@pytest.mark.parametrize("name,over,lmax", MANY_CASES, ids=[c[0] for c in MANY_CASES])
+def test_attention_many_sequences(name, over, lmax, form):
+    w = _small_w(1, **over)
+    rng = np.random.default_rng(8100 + len(name))
+    lens = rng.integers(0, lmax + 1, size=w.B).astype(np.int32)
+    lens[0] = lmax  # the longest sequence fixes lmax
+    lens[1] = 0
+    cap = lmax + 8
+    q, kc, vc, kt, vt, par, lens = _attn_case(w, lens, cap, 8200 + len(name))
+    rc, out, mk, st, sst = _run_attn(w, q, kc, vc, kt, vt, par, lens, form=form)
+    assert rc == 0 and (sst == 0).all()
+    orc, ref = oracle.attention(wl.as_f32(w, q), wl.as_f32(w, kc), wl.as_f32(w, vc), wl.as_f32(w, kt),
+                                wl.as_f32(w, vt), mk, lens, int(lens.max()), st)
+    H.check_attention(w, H.out_f32(w, out), ref, name)
+
+
 @pytest.mark.parametrize("form", FORMS[1:], ids=FORM_IDS[1:])
 def test_attention_deterministic_and_no_leakage(form):
     w = _small_w(1, B=2, dtype="bf16", Hq=8, Hkv=2, D=128, M=40)
