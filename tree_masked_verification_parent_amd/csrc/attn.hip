@@ -65,12 +65,13 @@ struct AttnDev {
   int32_t* seq_status;
   float* ws_o;   // split partials [B][Hkv][ns][R][D]; stream partials [2*grid][qb_rows][D]
   float* ws_ml;  // matching (m, l) pairs
-  int* ws_pref;  // stream form: tiles before each sequence, [B + 1]
+  int* ws_pref;  // stream form: tiles before each sequence [B + 1], then non-empty sequences before it [B + 1]
   int64_t cap;
   int B, T, Hq, Hkv, G, R, W;
   int lmax_bound, kc, ns, nqb, qb_rows, nunits;
   int n_slots;      // cache rows when slot is set
   int stream_grid;  // workgroups of the stream form
+  int piece_cost;   // stream form: key tiles' worth of time one unit's set-up and output cost
   float scale_log2;
 };
 
@@ -646,8 +647,9 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   __shared__ int s_pref[kStreamMaxB + 1];  // s_pref[b] = tiles of sequences < b (per unit)
   __shared__ int s_len[kStreamMaxB];
   __shared__ int s_row[kStreamMaxB];  // cache row of each sequence
-  __shared__ int s_wsum[NW + NP];
-  __shared__ int s_carry;
+  __shared__ int s_npref[kStreamMaxB + 1];  // non-empty sequences before b
+  __shared__ int s_wsum[NW + NP], s_wsum2[NW + NP];
+  __shared__ int s_carry, s_carry2;
   __shared__ uint64_t s_mask[NW * QMAX * 16][4];  // each lane's tree-mask words, its own rows only
 
   const int tid = threadIdx.x;
@@ -661,7 +663,9 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   // ---- per-sequence tile counts and their prefix (every workgroup computes it)
   if (tid == 0) {
     s_pref[0] = 0;
+    s_npref[0] = 0;
     s_carry = 0;
+    s_carry2 = 0;
   }
   __syncthreads();
   for (int base = 0; base < B; base += NT) {
@@ -672,19 +676,34 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
       s_len[b] = a.len[b];
       s_row[b] = a.slot ? a.slot[b] : b;
     }
-    int x = v;
+    int x = v, x2 = v > 0 ? 1 : 0;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
+      const int y = __shfl_up(x, o), y2 = __shfl_up(x2, o);
+      if (lane >= o) {
+        x += y;
+        x2 += y2;
+      }
     }
-    if (lane == 63) s_wsum[wave] = x;
+    if (lane == 63) {
+      s_wsum[wave] = x;
+      s_wsum2[wave] = x2;
+    }
     __syncthreads();
-    int off = s_carry;
-    for (int w = 0; w < wave; ++w) off += s_wsum[w];
-    if (b < B) s_pref[b + 1] = off + x;
+    int off = s_carry, off2 = s_carry2;
+    for (int w = 0; w < wave; ++w) {
+      off += s_wsum[w];
+      off2 += s_wsum2[w];
+    }
+    if (b < B) {
+      s_pref[b + 1] = off + x;
+      s_npref[b + 1] = off2 + x2;
+    }
     __syncthreads();
-    if (tid == NT - 1) s_carry = off + x;
+    if (tid == NT - 1) {
+      s_carry = off + x;
+      s_carry2 = off2 + x2;
+    }
     __syncthreads();
   }
   const int G = gridDim.x;
@@ -694,9 +713,32 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   const int c = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int UPB = a.Hkv * a.nqb;  // units per sequence
   const int64_t N = (int64_t)UPB * s_pref[B];
-  const int64_t lo = stream_lo(c, N, G), hi = stream_lo(c + 1, N, G);
+  // Ranges are equal in cost, not in tiles: a unit costs its key tiles plus
+  // piece_cost for its set-up and output, so a range that starts several
+  // units gets fewer tiles.  Cost position p maps to the stream tile it
+  // reaches (positions inside a unit's set-up map to its first tile).
+  const int PC = a.piece_cost;
+  auto seq_cost = [&](int b) { return (int64_t)UPB * ((int64_t)s_pref[b] + (int64_t)PC * s_npref[b]); };
+  const int64_t CT = seq_cost(B);
+  auto cost_to_tile = [&](int64_t p) -> int64_t {
+    if (p >= CT) return N;
+    int l = 0, h = B;
+    while (h - l > 1) {
+      const int m = (l + h) >> 1;
+      if (seq_cost(m) <= p) l = m;
+      else h = m;
+    }
+    const int ntl = s_pref[l + 1] - s_pref[l];
+    const int off = (int)(p - seq_cost(l));
+    const int j = off / (ntl + PC), r = off - j * (ntl + PC);
+    return (int64_t)UPB * s_pref[l] + (int64_t)j * ntl + max(0, r - PC);
+  };
+  const int64_t lo = cost_to_tile(stream_lo(c, CT, G)), hi = cost_to_tile(stream_lo(c + 1, CT, G));
   if (c == 0 && a.ws_pref)
-    for (int b = tid; b <= B; b += NT) a.ws_pref[b] = s_pref[b];
+    for (int b = tid; b <= B; b += NT) {
+      a.ws_pref[b] = s_pref[b];
+      a.ws_pref[B + 1 + b] = s_npref[b];
+    }
 
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.kcache);
@@ -1060,14 +1102,21 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   const int qb = u % a.nqb, bg = u / a.nqb;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int* pref = a.ws_pref;
+  const int* npref = a.ws_pref + a.B + 1;
   const int ntl = pref[b + 1] - pref[b];
   if (ntl == 0) return;
   const int UPB = a.Hkv * a.nqb;
-  const int64_t N = (int64_t)UPB * pref[a.B];
   const int G = a.stream_grid;
+  const int PC = a.piece_cost;
+  // The unit's cost interval is [CU, CU + PC + ntl): its set-up, then its
+  // tiles; the ranges are equal cuts of the total cost CT (as in the main
+  // kernel), and a range boundary at cost p inside the unit's tiles falls
+  // before tile P + (p - CU - PC).
+  const int64_t CT = (int64_t)UPB * ((int64_t)pref[a.B] + (int64_t)PC * npref[a.B]);
+  const int64_t CU = (int64_t)UPB * ((int64_t)pref[b] + (int64_t)PC * npref[b]) + (int64_t)(g * a.nqb + qb) * (ntl + PC);
   const int64_t P = (int64_t)UPB * pref[b] + (int64_t)(g * a.nqb + qb) * ntl;
   const int64_t E = P + ntl;
-  const int c0 = stream_range_of(P, N, G), c1 = stream_range_of(E - 1, N, G);
+  const int c0 = stream_range_of(CU + PC, CT, G), c1 = stream_range_of(CU + PC + ntl - 1, CT, G);
   if (c0 == c1) return;
   __shared__ int s_slot[kMaxPieces];
   __shared__ int s_np;
@@ -1088,9 +1137,14 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
       bool has = false;
       int slot = 0;
       if (cc <= c1) {
-        const int64_t hi_c = stream_lo(cc + 1, N, G);
-        has = stream_lo(cc, N, G) != hi_c;
-        slot = 2 * cc + ((cc < c1 || E == hi_c) ? 1 : 0);
+        // tiles of range cc inside the unit: [tlo, thi); the last range ends
+        // at the unit's end exactly when its cost end reaches no further
+        // than the next unit's first tile
+        const int64_t clo = stream_lo(cc, CT, G), chi = stream_lo(cc + 1, CT, G);
+        const int64_t tlo = cc == c0 ? P : P + (clo - CU - PC);
+        const int64_t thi = cc < c1 ? P + (chi - CU - PC) : E;
+        has = tlo < thi;
+        slot = 2 * cc + ((cc < c1 || chi <= CU + ntl + 2 * (int64_t)PC) ? 1 : 0);
       }
       const uint64_t bal = __ballot(has);
       const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
@@ -1359,6 +1413,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   p->R = p->G * p->T;
   p->nqt = (p->R + 15) / 16;
   p->grid = 0;
+  p->piece_cost = 0;
   // Key tiles the stream form would hold at most (host bound).
   const int64_t stream_tiles = (int64_t)a->B * a->Hkv * ((p->nqt + 11) / 12) *
                                (((int64_t)a->lmax_bound + KT - 1) / KT + (p->T + KT - 1) / KT);
@@ -1392,6 +1447,11 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->nwk = 1;
     p->stages = 4;
     p->qb_rows = tpb * 16;
+    // A unit boundary inside a range costs the compute waves about five key
+    // tiles' worth of time when nine or more of them store their pieces and
+    // load the next piece's inputs at once, less with fewer waves (measured
+    // per-tile stamps; range cuts balance tiles plus this per unit).
+    p->piece_cost = p->nw >= 9 ? 5 : p->nw >= 4 ? 2 : 0;
     // One workgroup per CU.
     if (cus <= 0) return false;
     p->grid = cus;
@@ -1410,7 +1470,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->kc = 0;
     p->ns = 1;
     const size_t rows = (size_t)2 * p->grid * p->qb_rows;
-    const size_t pref_bytes = (((size_t)a->B + 1) * sizeof(int) + 255) / 256 * 256;
+    const size_t pref_bytes = ((size_t)2 * (a->B + 1) * sizeof(int) + 255) / 256 * 256;
     p->ws_bytes = pref_bytes + rows * (a->D + 2) * sizeof(float);
     return true;
   }
@@ -1444,7 +1504,7 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.seq_status = a->seq_status;
   if (p.wide) {
     unsigned char* w = static_cast<unsigned char*>(a->workspace);
-    const size_t pref_bytes = (((size_t)a->B + 1) * sizeof(int) + 255) / 256 * 256;
+    const size_t pref_bytes = ((size_t)2 * (a->B + 1) * sizeof(int) + 255) / 256 * 256;
     d.ws_pref = reinterpret_cast<int*>(w);
     d.ws_o = reinterpret_cast<float*>(w + pref_bytes);
     d.ws_ml = d.ws_o + (size_t)2 * p.grid * p.qb_rows * a->D;
@@ -1456,6 +1516,7 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     d.ws_ml = ws ? ws + n_o : nullptr;
   }
   d.stream_grid = p.grid;
+  d.piece_cost = p.piece_cost;
   d.cap = a->cap;
   d.B = a->B;
   d.T = p.T;

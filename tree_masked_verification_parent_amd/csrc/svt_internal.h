@@ -28,6 +28,7 @@ struct AttnPlan {
   int nqb;           // query blocks per KV head
   int kc;            // prefix keys per split (multiple of 64)
   int ns;            // splits in the grid (upper bound; device len decides the rest)
+  int piece_cost;    // stream form: key tiles' worth of time a unit's set-up and output cost
   size_t ws_bytes;   // workspace bytes
 };
 bool plan_attention(const svt_attn_args* a, AttnPlan* p);
