@@ -168,9 +168,9 @@ typedef struct svt_attn_args {
  *   SVT_ATTN_AUTO    choose by shape
  *   SVT_ATTN_SPLIT   fixed key splits per (sequence, KV head); a sequence's
  *                    result does not depend on the rest of the batch
- *   SVT_ATTN_STREAM  the key tiles of the whole batch cut into one equal
- *                    range per compute unit (needs bf16 and B <= 1024, else
- *                    SVT_ERR_UNSUPPORTED) */
+ *   SVT_ATTN_STREAM  the key tiles of the whole batch cut into one range of
+ *                    equal cost per compute unit (needs bf16 and B <= 1024,
+ *                    else SVT_ERR_UNSUPPORTED) */
 typedef enum svt_attn_form { SVT_ATTN_AUTO = 0, SVT_ATTN_SPLIT = 1, SVT_ATTN_STREAM = 2 } svt_attn_form;
 
 /* Bytes of workspace svt_verify_attention needs for these shapes (pointer

@@ -14,9 +14,9 @@
 // query tiles.  Two decompositions compute the same function:
 //   * stream form (attn_bf16_stream_kernel + attn_stream_combine_kernel): the
 //     64-key tiles of all (sequence, KV head, query block) units form one
-//     stream cut into one equal range per CU; compute waves own one query tile
-//     each, two producer waves stream K and V tiles HBM -> LDS; units cut by
-//     range ends leave (m, l, O) partials merged in stream order.
+//     stream cut into one range of equal cost per CU; compute waves own one
+//     query tile each, two producer waves stream K and V tiles HBM -> LDS;
+//     units cut by range ends leave (m, l, O) partials merged in stream order.
 //   * split form (attn_bf16_kernel + attn_combine_kernel): one workgroup per
 //     (sequence, KV head, query block, prefix split of kc keys); the last split
 //     also takes the tree keys; splits are merged in split order.
@@ -595,8 +595,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 // query tiles of 16 rows, one per compute wave, so every K/V tile of the unit
 // crosses HBM -> LDS once and feeds all of its query rows.  A unit's key tiles
 // are its prefix tiles followed by its tree tiles; the tiles of all units,
-// concatenated in unit order, form one stream that is cut into gridDim.x equal
-// ranges, one per workgroup (one workgroup per CU).  A workgroup walks its
+// concatenated in unit order, form one stream that is cut into gridDim.x
+// ranges of equal cost (tiles plus a set-up cost per unit), one per workgroup
+// (one workgroup per CU).  A workgroup walks its
 // range with one 4-deep DMA ring that runs across unit boundaries, fed by two
 // producer waves (one copies the K planes, the other the V planes) that do no
 // arithmetic: copies that stall on issue under memory back-pressure never hold
