@@ -875,15 +875,38 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     constexpr int NQ = decltype(nq_c)::value;
     const unsigned char* kl = lds + ((y - lo) % kStages) * TL::STAGEB;
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
+    for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
       for (int u = 0; u < 4; ++u) sacc[qt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NW * QMAX <= 9) {
+      // K fragments eight at a time: their LDS reads are in flight together
+      // before the first of their MFMAs waits, instead of one read and one
+      // wait per MFMA (the 12-wave form has no registers to spare for this)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int kb = 0; kb < NKS; kb += 2) {
+        bf16x8 kf[2][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          sacc[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              *reinterpret_cast<const bf16x8*>(kl + 16 * u * TL::ROWB + koff[ks]), qf[qt][ks], sacc[qt][u], 0, 0, 0);
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            kf[k2][u] = *reinterpret_cast<const bf16x8*>(kl + 16 * u * TL::ROWB + koff[kb + k2]);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              sacc[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k2][u], qf[qt][kb + k2], sacc[qt][u], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            sacc[qt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                *reinterpret_cast<const bf16x8*>(kl + 16 * u * TL::ROWB + koff[ks]), qf[qt][ks], sacc[qt][u], 0, 0, 0);
     }
   };
   // Mask, softmax and P V of stream tile y from its scores.
