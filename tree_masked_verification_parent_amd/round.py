@@ -47,6 +47,12 @@ class VerifyRound:
         acc = self._accept_args()
         self.accept_ws = torch.empty(max(1, svt.svt_accept_workspace(acc)), dtype=torch.uint8, device=dev)
         self._attn_ws = None
+        # Argument structs are built once and reused: the tensors above are
+        # filled in place, never rebound, so their pointers stay valid.  (Per
+        # call, building them costs more host time than a short kernel takes.)
+        self._attn_cache = {}
+        self._accept_cache = None
+        self._commit_cache = None
 
     # ---- argument structs -------------------------------------------------
     def _attn_args(self, layer: int):
@@ -68,22 +74,31 @@ class VerifyRound:
     def set_lmax_bound(self, bound: int):
         """Host upper bound of the batch length; sizes the attention grid."""
         self.lmax_bound = int(bound)
+        self._attn_cache = {}
         need = svt.svt_verify_attention_workspace(self._attn_args(0))
         if need and (self._attn_ws is None or self._attn_ws.numel() < need):
             self._attn_ws = torch.empty(need, dtype=torch.uint8, device=self.q.device)
+        self._attn_cache = {}
 
     # ---- the four calls -----------------------------------------------------
     def build_mask(self, flags: int = 0) -> int:
         return svt.svt_build_mask(self.parents, self.M, self.mask, self.depth, self.status, flags)
 
     def attention(self, layer: int = 0) -> int:
-        return svt.svt_verify_attention(self._attn_args(layer))
+        a = self._attn_cache.get(layer)
+        if a is None:
+            a = self._attn_cache[layer] = self._attn_args(layer)
+        return svt.svt_verify_attention(a)
 
     def accept(self) -> int:
-        return svt.svt_accept(self._accept_args())
+        if self._accept_cache is None:
+            self._accept_cache = self._accept_args()
+        return svt.svt_accept(self._accept_cache)
 
     def commit(self, flags: int = 0) -> int:
-        return svt.svt_commit(self._commit_args(), flags)
+        if self._commit_cache is None:
+            self._commit_cache = self._commit_args()
+        return svt.svt_commit(self._commit_cache, flags)
 
     def step(self) -> int:
         """One full round: mask, attention over every attention layer, accept, commit."""
