@@ -1113,15 +1113,15 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
 // Grid (unit, group of rows): D / DPT threads per row, DPT dims each (the
 // launch picks DPT so that the grid covers the chip).  The first wave lists
 // the unit's pieces (their partial slots, empty ranges skipped) in LDS, one
-// range per lane; the partials of KB pieces are loaded before any of them is
-// merged.  Units inside a single range return at once.
+// range per lane; the partials of KB = 32 / DPT pieces are loaded before any
+// of them is merged.  Units inside a single range return at once.
 constexpr int kMaxPieces = 64;  // pieces listed per pass (one wave)
 
 template <int D, int DPT>
 __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   constexpr int TPR = D / DPT;   // threads per row
   constexpr int RPW = 256 / TPR; // rows per workgroup
-  constexpr int KB = 4;        // pieces loaded per batch
+  constexpr int KB = 32 / DPT;  // pieces loaded per batch
   const int u = blockIdx.x;
   const int qb = u % a.nqb, bg = u / a.nqb;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
@@ -1182,8 +1182,9 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
       float mi[KB], li[KB], oi[KB][DPT];
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
-        if (k + j >= np) break;
-        const int64_t pr = (int64_t)s_slot[k + j] * a.qb_rows + rl;
+        // every slot loads (past the last piece: the last piece again), so the
+        // batch's loads issue back to back; only the real pieces are merged
+        const int64_t pr = (int64_t)s_slot[min(k + j, np - 1)] * a.qb_rows + rl;
         mi[j] = a.ws_ml[pr * 2];
         li[j] = a.ws_ml[pr * 2 + 1];
         const float* src = a.ws_o + pr * D + d0;
