@@ -638,8 +638,11 @@ def main():
     depth = r.depth.cpu().numpy()
 
     stream = torch.cuda.current_stream()
-    n_ev = 4 + L
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)] for _ in range(args.steps)]
+    # five events per step: before the mask, after it, after the last
+    # attention layer, after accept, after commit (the mean per attention layer
+    # is the attention interval over L: per-layer events would give the same
+    # mean and cost host time on the launch-bound small rounds)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 
     def one_step(ev=None):
         r.len.copy_(len0)
@@ -651,14 +654,14 @@ def main():
             ev[1].record(stream)
         for layer in range(L):
             rc = rc or r.attention(layer)
-            if ev:
-                ev[2 + layer].record(stream)
+        if ev:
+            ev[2].record(stream)
         rc = rc or r.accept()
         if ev:
-            ev[2 + L].record(stream)
+            ev[3].record(stream)
         rc = rc or r.commit()
         if ev:
-            ev[3 + L].record(stream)
+            ev[4].record(stream)
         return rc
 
     for _ in range(args.warmup):
@@ -676,10 +679,9 @@ def main():
         return float(np.mean([evs[k][i].elapsed_time(evs[k][j]) for k in range(args.steps)])) * 1e-3
 
     t_mask = dur(0, 1)
-    t_attn_layers = [dur(1 + l, 2 + l) for l in range(L)]
-    t_attn = float(np.mean(t_attn_layers))
-    t_accept = dur(1 + L, 2 + L)
-    t_commit = dur(2 + L, 3 + L)
+    t_attn = dur(1, 2) / L
+    t_accept = dur(2, 3)
+    t_commit = dur(3, 4)
     ms_per_step = elapsed / args.steps * 1e3
 
     attn_bytes = algorithmic_bytes_attention(w, lens0, w.T)
