@@ -211,13 +211,13 @@ def cpu_baseline(w, parents, lens, logits, tokens, seed, budget_s):
     al, path, _ = oracle.accept(am, tokens, parents, w.M, st)
     t_accept = time.perf_counter() - t0
     # attention: whole sequences of one layer, in a seeded order, until the
-    # sample (inputs included) has used about half the budget
+    # sample (inputs included) has used about 80 % of the budget
     order = np.argsort(gen.u64(gen.stream_key(seed, 991), w.B))
     picked, t_attn_sample, keys_sample = [], 0.0, 0
     t_part = time.perf_counter()
     sub = wl.Workload(**{**w.__dict__, "B": 1})
     for b in order:
-        if picked and time.perf_counter() - t_part > 0.5 * budget_s:
+        if picked and time.perf_counter() - t_part > 0.8 * budget_s:
             break
         Lb = int(lens[b])
         q, kc, vc, kt, vt = wl.attention_inputs(sub, np.array([Lb], np.int32), Lb, seed + 1000 + int(b),
