@@ -227,12 +227,17 @@ bool plan_accept(const svt_accept_args* a, AcceptPlan* p) {
   if (!a || a->B < 0 || a->M < 0 || a->M >= SVT_MAX_T || a->V <= 0) return false;
   const int T = a->M + 1;
   p->rows = a->B * T;
-  // Enough workgroups to cover the chip (about 2048), chunks of >= 4096 entries.
+  // Chunks of >= 4096 entries, enough workgroups for about one wave over the
+  // chip (~2048), but no chunk above 5120 entries (20 KB): with many rows the
+  // first two rules give a few very long workgroups per row, and the last of
+  // them run alone.
   int nchunk = 1;
   if (p->rows > 0) {
     const int by_size = (a->V + 4095) / 4096;
     const int by_par = (2048 + p->rows - 1) / p->rows;
+    const int by_cap = (a->V + 5119) / 5120;
     nchunk = by_size < by_par ? by_size : by_par;
+    if (nchunk < by_cap) nchunk = by_cap;
     if (nchunk < 1) nchunk = 1;
   }
   int chunk = (a->V + nchunk - 1) / nchunk;
