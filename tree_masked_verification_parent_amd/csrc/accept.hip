@@ -227,10 +227,10 @@ bool plan_accept(const svt_accept_args* a, AcceptPlan* p) {
   if (!a || a->B < 0 || a->M < 0 || a->M >= SVT_MAX_T || a->V <= 0) return false;
   const int T = a->M + 1;
   p->rows = a->B * T;
-  // Chunks of >= 4096 entries, enough workgroups for about one wave over the
-  // chip (~2048), but no chunk above 5120 entries (20 KB): with many rows the
-  // first two rules give a few very long workgroups per row, and the last of
-  // them run alone.
+  // The fewer of: chunks of >= 4096 entries, or enough workgroups for about
+  // one wave over the chip (~2048); then more chunks if needed so that none
+  // exceeds 5120 entries (20 KB): with many rows the first rule alone gives a
+  // few very long workgroups per row, and the last of them run alone.
   int nchunk = 1;
   if (p->rows > 0) {
     const int by_size = (a->V + 4095) / 4096;
