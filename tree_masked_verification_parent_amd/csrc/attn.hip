@@ -1474,9 +1474,10 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->qb_rows = tpb * 16;
     // A unit boundary inside a range costs the compute waves about five key
     // tiles' worth of time when nine or more of them store their pieces and
-    // load the next piece's inputs at once, less with fewer waves (measured
-    // per-tile stamps; range cuts balance tiles plus this per unit).
-    p->piece_cost = p->nw >= 9 ? 5 : p->nw >= 4 ? 2 : 0;
+    // load the next piece's inputs at once, about two with fewer waves
+    // (per-tile stamps for nine and more; call times over 0..4 for the one-
+    // and two-tile forms); range cuts balance tiles plus this per unit.
+    p->piece_cost = p->nw >= 9 ? 5 : 2;
     // One workgroup per CU.
     if (cus <= 0) return false;
     p->grid = cus;
