@@ -350,6 +350,10 @@ ATTN_CASES = [
     ("bf16-lenzero", dict(B=2, dtype="bf16", Hq=8, Hkv=4, D=128, M=12), [0, 0]),
     ("bf16-gqa8-qw3", dict(B=2, dtype="bf16", Hq=16, Hkv=2, D=128, M=20), [4100, 999]),
     ("bf16-gqa4-qw2", dict(B=2, dtype="bf16", Hq=8, Hkv=2, D=128, M=24), [3000, 2999]),
+    # 3 and 5-6 query tiles per KV head: the four- and six-wave stream forms
+    ("bf16-d128-gqa4-3tiles", dict(B=3, dtype="bf16", Hq=8, Hkv=2, D=128, M=11), [1000, 64, 301]),
+    ("bf16-d64-gqa4-5tiles", dict(B=2, dtype="bf16", Hq=8, Hkv=2, D=64, M=16), [2000, 129]),
+    ("bf16-d128-gqa2-6tiles", dict(B=2, dtype="bf16", Hq=4, Hkv=2, D=128, M=47), [777, 1500]),
 ]
 
 
