@@ -354,6 +354,10 @@ ATTN_CASES = [
     ("bf16-d128-gqa4-3tiles", dict(B=3, dtype="bf16", Hq=8, Hkv=2, D=128, M=11), [1000, 64, 301]),
     ("bf16-d64-gqa4-5tiles", dict(B=2, dtype="bf16", Hq=8, Hkv=2, D=64, M=16), [2000, 129]),
     ("bf16-d128-gqa2-6tiles", dict(B=2, dtype="bf16", Hq=4, Hkv=2, D=128, M=47), [777, 1500]),
+    # head dim 64 with 2, 4 and 12 query tiles per KV head (the other D=64 stream forms)
+    ("bf16-d64-mha-2tiles", dict(B=3, dtype="bf16", Hq=2, Hkv=2, D=64, M=20), [650, 3, 1200]),
+    ("bf16-d64-gqa2-4tiles", dict(B=2, dtype="bf16", Hq=4, Hkv=2, D=64, M=31), [900, 2500]),
+    ("bf16-d64-gqa16-12tiles", dict(B=2, dtype="bf16", Hq=16, Hkv=1, D=64, M=11), [1700, 400]),
 ]
 
 
