@@ -60,7 +60,7 @@ typedef enum svt_status {
   SVT_ERR_TREE_RANGE = -4,   /* some parents[b][i], i >= 1, outside [0, M] or == i     */
   SVT_ERR_TREE_CYCLE = -5,   /* some node's parent chain never reaches row 0           */
   SVT_ERR_CAPACITY = -6,     /* commit would need more than cap cache columns          */
-  SVT_ERR_WORKSPACE = -7,    /* workspace pointer missing or too small                 */
+  SVT_ERR_WORKSPACE = -7,    /* workspace pointer missing, too small or misaligned     */
   SVT_ERR_HIP = -8,          /* a HIP runtime call failed                               */
   SVT_ERR_LENGTH = -9        /* device lengths inconsistent (len > lmax, lmax > bound)  */
 } svt_status;
@@ -155,7 +155,8 @@ typedef struct svt_attn_args {
   int32_t* seq_status;       /* [B] out, or NULL: SVT_OK, the tree status, or         */
                              /* SVT_ERR_LENGTH if 0 <= len[b] <= lmax <= lmax_bound   */
                              /* fails.  Such sequences get all-zero output.           */
-  void* workspace;           /* device scratch, svt_verify_attention_workspace bytes  */
+  void* workspace;           /* device scratch, svt_verify_attention_workspace bytes, */
+                             /* 16-byte aligned (else SVT_ERR_WORKSPACE)               */
   size_t workspace_bytes;
   int32_t form;              /* svt_attn_form: which work decomposition (bf16 only)   */
   const int32_t* seq_slot;   /* [B] cache row of each sequence, or NULL (row b)        */
@@ -206,7 +207,8 @@ typedef struct svt_accept_args {
   int32_t* accept_len;         /* [B] out                                            */
   int32_t* path;               /* [B][T] out (the path_indices of the commit)        */
   int32_t* bonus;              /* [B] out                                            */
-  void* workspace;             /* device scratch, svt_accept_workspace bytes         */
+  void* workspace;             /* device scratch, svt_accept_workspace bytes,        */
+                               /* 8-byte aligned (else SVT_ERR_WORKSPACE)            */
   size_t workspace_bytes;
 } svt_accept_args;
 

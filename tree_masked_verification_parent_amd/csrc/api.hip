@@ -203,7 +203,7 @@ const char* svt_status_string(int code) {
     case SVT_ERR_TREE_RANGE: return "tree: parent index out of [0, M] or self-parent";
     case SVT_ERR_TREE_CYCLE: return "tree: a parent chain never reaches the root";
     case SVT_ERR_CAPACITY: return "commit exceeds cache capacity";
-    case SVT_ERR_WORKSPACE: return "workspace missing or too small";
+    case SVT_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case SVT_ERR_HIP: return "HIP runtime error";
     case SVT_ERR_LENGTH: return "inconsistent sequence lengths";
     default: return "unknown status";
