@@ -476,6 +476,56 @@ def test_attention_invalid_sequences_and_length_errors(form):
     assert rc == 0 and (sst == svt.SVT_ERR_LENGTH).all() and not H.out_f32(w, out).any()
 
 
+def test_workspace_missing_small_or_misaligned_is_rejected():
+    """Attention needs a 16-byte aligned workspace of svt_verify_attention_workspace
+    bytes and accept an 8-byte aligned one of svt_accept_workspace bytes; anything
+    else returns SVT_ERR_WORKSPACE before a kernel is launched."""
+    w = _small_w(1, B=2, dtype="bf16", Hq=8, Hkv=2, D=128, M=8)
+    q, kc, vc, kt, vt, par, lens = _attn_case(w, [300, 41], 340, 7450)
+    tq = H.to_dev(q)
+    mk = torch.zeros(2, 9, 1, dtype=torch.int64, device=DEV)
+    dp = torch.zeros(2, 9, dtype=torch.int32, device=DEV)
+    st = torch.zeros(2, dtype=torch.int32, device=DEV)
+    assert svt.svt_build_mask(_i32(par), 8, mk, dp, st) == 0
+    out = torch.empty_like(tq)
+    a = svt.attn_args(tq, H.to_dev(kc), H.to_dev(vc), _i32(lens), _i32([300]), 300, H.to_dev(kt), H.to_dev(vt),
+                      mk, out, status=st, form=svt.SVT_ATTN_STREAM)
+    need = svt.svt_verify_attention_workspace(a)
+    assert need > 0
+    ws = torch.empty(need + 64, dtype=torch.uint8, device=DEV)
+    base = ws.data_ptr()
+    print("attention workspace checks", flush=True)
+    assert svt.svt_verify_attention(a) == svt.SVT_ERR_WORKSPACE  # none
+    a.workspace, a.workspace_bytes = base, need - 1
+    assert svt.svt_verify_attention(a) == svt.SVT_ERR_WORKSPACE  # too small
+    a.workspace, a.workspace_bytes = base + 8, need
+    assert svt.svt_verify_attention(a) == svt.SVT_ERR_WORKSPACE  # 8-byte aligned only
+    a.workspace, a.workspace_bytes = base + 16, need
+    assert svt.svt_verify_attention(a) == svt.SVT_OK
+    torch.cuda.synchronize()
+
+    logits = np.random.default_rng(7451).standard_normal((2, 9, 1000)).astype(np.float32)
+    lg = torch.as_tensor(logits, device=DEV)
+    tk = _i32(np.zeros((2, 9)))
+    am, path = (torch.zeros(2, 9, dtype=torch.int32, device=DEV) for _ in range(2))
+    al, bo = (torch.zeros(2, dtype=torch.int32, device=DEV) for _ in range(2))
+    acc = svt.accept_args(lg, tk, _i32(par), mk, dp, am, al, path, bo, status=st)
+    need = svt.svt_accept_workspace(acc)
+    wsa = torch.empty(need + 64, dtype=torch.uint8, device=DEV)
+    base = wsa.data_ptr()
+    print("accept workspace checks", flush=True)
+    assert svt.svt_accept(acc) == svt.SVT_ERR_WORKSPACE
+    acc.workspace, acc.workspace_bytes = base, need - 1
+    assert svt.svt_accept(acc) == svt.SVT_ERR_WORKSPACE
+    acc.workspace, acc.workspace_bytes = base + 4, need
+    assert svt.svt_accept(acc) == svt.SVT_ERR_WORKSPACE
+    acc.workspace, acc.workspace_bytes = base + 8, need
+    assert svt.svt_accept(acc) == svt.SVT_OK
+    torch.cuda.synchronize()
+    al_ref, _, _ = oracle.accept(oracle.argmax(logits), np.zeros((2, 9), np.int32), par, 8, np.zeros(2, np.int32))
+    assert np.array_equal(H.from_dev(al), al_ref)
+
+
 def test_attention_host_argument_errors():
     w = _small_w(1, B=1, dtype="bf16", Hq=4, Hkv=2, D=128, M=4)
     q, kc, vc, kt, vt, par, lens = _attn_case(w, [10], 16, 7400)
