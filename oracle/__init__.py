@@ -119,6 +119,82 @@ def attention_row(q_row, k_cache_bh, v_cache_bh, k_tree_bh, v_tree_bh, mask_row,
     return out
 
 
+def default_threads() -> int:
+    """Threads for the row-parallel drivers: the host's cores, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def attention_rows(q, k_cache, v_cache, k_tree, v_tree, mk, lens, lmax: int, rows, scale: float | None = None,
+                   threads: int | None = None, to_f32=None):
+    """oracle_attention_row for the listed (b, i, h) rows, run on `threads`
+    threads (ctypes releases the GIL during each call; the C function keeps
+    no shared state).  Array inputs in the layouts of `attention`: float32
+    (exact upcasts), or any dtype that `to_f32` maps exactly to float32 (it is
+    applied to each (sequence, KV head) slab and query row as it is used, so
+    a large bf16 cache is never upcast whole).  Returns float64
+    [len(rows)][D].  Every row is computed by the same single-threaded C
+    routine; the threads only run rows side by side."""
+    import concurrent.futures as cf
+
+    B, T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    sc = (1.0 / np.sqrt(D)) if scale is None else float(scale)
+    mk = _c(mk, np.uint64)
+    out = np.zeros((len(rows), D), dtype=np.float64)
+    groups: dict = {}
+    for k, (b, i, h) in enumerate(rows):
+        groups.setdefault((int(b), int(h) // G), []).append((k, int(i), int(h)))
+
+    f = (lambda x: x) if to_f32 is None else to_f32
+    import threading
+
+    n = default_threads() if threads is None else max(1, int(threads))
+    # tasks: chunks of one group's rows, enough of them to keep every thread busy
+    per = max(1, -(-n // max(1, len(groups))))
+    tasks = []
+    for key, lst in groups.items():
+        step = max(1, -(-len(lst) // per))
+        for s0 in range(0, len(lst), step):
+            tasks.append((key, lst[s0:s0 + step]))
+    left = {key: sum(1 for k2, _ in tasks if k2 == key) for key in groups}
+    slabs: dict = {}
+    locks = {key: threading.Lock() for key in groups}
+
+    def get_slabs(key):
+        # each (sequence, KV head) slab is converted once and dropped after its last chunk
+        with locks[key]:
+            if key not in slabs:
+                b, g = key
+                slabs[key] = tuple(_c(f(x[b, g]), np.float32) for x in (k_cache, v_cache, k_tree, v_tree))
+            return slabs[key]
+
+    def done(key):
+        with locks[key]:
+            left[key] -= 1
+            if left[key] == 0:
+                slabs.pop(key, None)
+
+    def run(task):
+        key, lst = task
+        b, _ = key
+        kc, vc, kt, vt = get_slabs(key)
+        for k, i, h in lst:
+            qr = _c(f(q[b, i, h]), np.float32)
+            lib().oracle_attention_row(_p(qr), _p(kc), _p(vc), _p(kt), _p(vt), _p(mk[b, i]), int(lens[b]),
+                                       int(lmax), T, D, sc, _p(out[k]))
+        done(key)
+
+    lib()  # load once, before any thread calls it
+    if n == 1:
+        for t in tasks:
+            run(t)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(run, tasks))
+    return out
+
+
 def argmax(logits: np.ndarray):
     x = _c(logits, np.float32)
     V = x.shape[-1]

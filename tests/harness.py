@@ -95,3 +95,155 @@ def check_attention(w: wl.Workload, got: np.ndarray, ref: np.ndarray, what: str 
     assert err <= tol, f"{what}: max-abs error {err:.3e} > {tol:.1e}"
     assert err <= norm, f"{what}: max-abs error {err:.3e} > normalised bound {norm:.3e}"
     return err
+
+
+# --------------------------------------------------------------------------
+# Where the stream form of svt_verify_attention cuts the batch.  The kernel
+# concatenates the key tiles of every (sequence, KV head, query block) unit
+# (prefix tiles, then tree tiles) and gives each of `grid` workgroups one
+# range of equal cost, a unit costing its tiles plus a set-up charge.  This
+# mirrors that rule on the host so that a test can put inputs right after a
+# cut; the expected values still come from the oracle alone.
+# --------------------------------------------------------------------------
+KT = 64
+
+
+@dataclasses.dataclass
+class StreamUnit:
+    b: int
+    g: int
+    qb: int
+    base: int          # first stream tile
+    ntl: int           # tiles (prefix + tree)
+    n_prefix: int      # prefix tiles
+    row_lo: int        # query rows [row_lo, row_hi) of the KV head (r = hl * T + i)
+    row_hi: int
+    cuts: list         # stream tiles inside (base, base + ntl) where a range starts
+
+
+def stream_plan(B, T, Hq, Hkv, lens, status=None):
+    """(nqb, qb_rows, compute waves, set-up charge) of the stream form."""
+    R = (Hq // Hkv) * T
+    nqt = (R + 15) // 16
+    nqb0 = (nqt + 11) // 12
+    tpb = (nqt + nqb0 - 1) // nqb0
+    nw = tpb if tpb <= 2 else 4 if tpb <= 4 else 6 if tpb <= 6 else 9 if tpb <= 9 else 12
+    pc = 5 if nw >= 9 else 2
+    qb_rows = tpb * 16
+    nqb = (R + qb_rows - 1) // qb_rows
+    return nqb, qb_rows, nw, pc
+
+
+def stream_units(B, T, Hq, Hkv, lens, grid, status=None):
+    """Units of the stream form in stream order, each with the range starts
+    that fall strictly inside it (a unit with cuts is merged from partials)."""
+    G = Hq // Hkv
+    R = G * T
+    nqb, qb_rows, nw, pc = stream_plan(B, T, Hq, Hkv, lens, status)
+    ntree = (T + KT - 1) // KT
+    tiles = []
+    for b in range(B):
+        ok = status is None or int(status[b]) == 0
+        tiles.append((int(lens[b]) + KT - 1) // KT + ntree if ok else 0)
+    pref = [0]
+    npref = [0]
+    for b in range(B):
+        pref.append(pref[-1] + tiles[b])
+        npref.append(npref[-1] + (1 if tiles[b] > 0 else 0))
+    upb = Hkv * nqb
+    N = upb * pref[B]
+
+    def seq_cost(b):
+        return upb * (pref[b] + pc * npref[b])
+
+    CT = seq_cost(B)
+
+    def cost_to_tile(p):
+        if p >= CT:
+            return N
+        lo, hi = 0, B
+        while hi - lo > 1:
+            m = (lo + hi) // 2
+            if seq_cost(m) <= p:
+                lo = m
+            else:
+                hi = m
+        ntl = pref[lo + 1] - pref[lo]
+        off = p - seq_cost(lo)
+        j, r = divmod(off, ntl + pc)
+        return upb * pref[lo] + j * ntl + max(0, r - pc)
+
+    starts = sorted({cost_to_tile((c * CT) // grid) for c in range(grid)})
+    units = []
+    for b in range(B):
+        ntl = tiles[b]
+        if ntl == 0:
+            continue
+        for j in range(upb):
+            base = upb * pref[b] + j * ntl
+            g, qb = divmod(j, nqb)
+            cuts = [x for x in starts if base < x < base + ntl]
+            units.append(StreamUnit(b, g, qb, base, ntl, ntl - ntree, qb * qb_rows, min(R, (qb + 1) * qb_rows), cuts))
+    return units
+
+
+def run_attention(q, kc, vc, kt, vt, parents, lens, lmax_bound=None, status=None, scale=0.0, form=0, dev="cuda"):
+    """svt_build_mask then svt_verify_attention on host arrays (bf16 as uint16
+    bits).  The mask and tree status handed back for the comparison are the
+    oracle's own, built from the parent arrays, after asserting that the GPU's
+    equal them bit for bit; `status`, when given, overrides the tree status
+    that attention sees (and is handed back).  Returns (rc, out tensor, mask,
+    status, seq_status)."""
+    from tree_masked_verification_parent_amd import svt
+
+    def i32(x):
+        return torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device=dev)
+
+    lens = np.asarray(lens, np.int32)
+    lmax = int(lens.max()) if len(lens) else 0
+    B, T = parents.shape
+    M = T - 1
+    Wd = (T + 63) // 64
+    mk = torch.zeros(B, T, Wd, dtype=torch.int64, device=dev)
+    dp = torch.zeros(B, T, dtype=torch.int32, device=dev)
+    st_mask = torch.zeros(B, dtype=torch.int32, device=dev)
+    assert svt.svt_build_mask(i32(parents), M, mk, dp, st_mask) == 0
+    st = st_mask if status is None else i32(status)
+    tq, tkc, tvc, tkt, tvt = (to_dev(x, dev=dev) for x in (q, kc, vc, kt, vt))
+    out = torch.full(tq.shape, float("nan"), dtype=tq.dtype, device=dev)
+    sst = torch.full((B,), 55, dtype=torch.int32, device=dev)
+    ln_t, lm_t = i32(lens), i32([lmax])
+    bound = lmax if lmax_bound is None else lmax_bound
+    args = svt.attn_args(tq, tkc, tvc, ln_t, lm_t, bound, tkt, tvt, mk, out, status=st, seq_status=sst,
+                         scale=scale, form=form)
+    need = svt.svt_verify_attention_workspace(args)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = svt.attn_args(tq, tkc, tvc, ln_t, lm_t, bound, tkt, tvt, mk, out, status=st, seq_status=sst,
+                         scale=scale, workspace=ws, form=form)
+    rc = svt.svt_verify_attention(args)
+    torch.cuda.synchronize()
+    _, ost = oracle.validate(parents, M)
+    omk, _ = oracle.mask(parents, M, ost)
+    assert np.array_equal(from_dev(mk).view(np.uint64), omk), "GPU mask differs from the oracle's"
+    assert np.array_equal(from_dev(st_mask), ost), "GPU tree status differs from the oracle's"
+    return rc, out, omk, (ost if status is None else np.asarray(status, np.int32)), from_dev(sst)
+
+
+def accept_chunking(rows: int, V: int):
+    """(chunks per row, entries per chunk) of svt_accept's argmax pass, as its
+    plan cuts a row: the fewer of chunks of >= 4096 entries and ~2048
+    workgroups over the chip, then more chunks so none exceeds 5120 entries,
+    chunk length rounded up to a multiple of 4."""
+    nchunk = 1
+    if rows > 0:
+        by_size = (V + 4095) // 4096
+        by_par = (2048 + rows - 1) // rows
+        by_cap = (V + 5119) // 5120
+        nchunk = max(min(by_size, by_par), by_cap, 1)
+    chunk = (V + nchunk - 1) // nchunk
+    chunk = (chunk + 3) & ~3
+    return (V + chunk - 1) // chunk, chunk
+
+
+def cu_count(dev=0) -> int:
+    return int(torch.cuda.get_device_properties(dev).multi_processor_count)

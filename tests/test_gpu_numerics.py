@@ -1,0 +1,270 @@
+"""GPU parity on numerically hard inputs, against the oracle alone.
+
+- Sharp softmax: bf16 Q and K drawn at sigma 1 and 2 without the 1/sqrt(D)
+  factor, so the scaled scores spread over several units and a few keys
+  dominate every row (the generators' default makes the softmax nearly
+  uniform).  V stays at sigma 1/2: with outputs of magnitude 4 or more, the
+  rounding of the bf16 output alone (half an ulp = 2^-6) would exceed the
+  2e-2 max-abs contract whatever the kernel does.
+- Planted large scores: a key row set to a large multiple of one query row
+  gives that row a score about 50 (base-2 units) above the rest, placed in the
+  last prefix tile, in a tree row on the node's root path, in the first tile of
+  every cut of the stream form (so the lazy rescale of the running maximum and
+  the partial merge both see a late, large maximum), and in the very first
+  prefix tile (the later pieces then merge in with far smaller maxima).
+- Cross-chunk argmax: the argmax pass cuts a row of logits into chunks;
+  maxima duplicated in two chunks, ties across a chunk boundary, NaN in two
+  chunks, -0.0 / +0.0 in different chunks, all -inf rows, at vocabularies of
+  32000 (and 32003, no 16-byte loads) and 151552 entries.  Expected indices
+  are stated by construction and checked against the oracle.
+
+The masks and tree statuses the oracle uses come from the oracle
+(harness.run_attention asserts that the GPU's are equal bit for bit).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import harness as H
+import oracle
+from synth import gen
+from synth import workloads as wl
+from tree_masked_verification_parent_amd import svt
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+FORMS = [svt.SVT_ATTN_SPLIT, svt.SVT_ATTN_STREAM]
+FORM_IDS = ["split", "stream"]
+
+
+def _w(**kw):
+    return dataclasses.replace(wl.workload(1), dtype="bf16", **kw)
+
+
+def _inputs(w, lens, cap, seed, sigma_qk, sigma_v):
+    """Q, K caches and tree K at sigma_qk; V caches and tree V at sigma_v."""
+    q, kc, _, kt, _ = wl.attention_inputs(dataclasses.replace(w, qkv_sigma=sigma_qk), lens, cap, seed)
+    _, _, vc, _, vt = wl.attention_inputs(dataclasses.replace(w, qkv_sigma=sigma_v), lens, cap, seed + 7)
+    return q, kc, vc, kt, vt
+
+
+def _check(w, q, kc, vc, kt, vt, par, lens, form, what):
+    rc, out, mk, st, sst = H.run_attention(q, kc, vc, kt, vt, par, lens, form=form)
+    assert rc == 0 and (sst == 0).all(), (rc, sst)
+    f = lambda x: wl.as_f32(w, x)
+    _, ref = oracle.attention(f(q), f(kc), f(vc), f(kt), f(vt), mk, lens, int(lens.max()), st)
+    err = H.check_attention(w, H.out_f32(w, out), ref, what)
+    return ref, err
+
+
+SHARP_CASES = [
+    # name, shape, prefix lengths; together they cover the stream forms with
+    # 2, 4, 9 and 12 compute waves and both head dims
+    ("mha-d64-2tiles", dict(B=3, Hq=2, Hkv=2, D=64, M=20), [650, 3, 1200]),
+    ("gqa4-3tiles", dict(B=3, Hq=8, Hkv=2, D=128, M=11), [1000, 64, 301]),
+    ("gqa4-M32-9tiles", dict(B=4, Hq=32, Hkv=8, D=128, M=32), [3000, 1500, 2047, 777]),
+    ("gqa8-M20-11tiles", dict(B=2, Hq=16, Hkv=2, D=128, M=20), [4100, 999]),
+]
+
+
+@pytest.mark.parametrize("sigma", [1.0, 2.0])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("name,over,lens", SHARP_CASES, ids=[c[0] for c in SHARP_CASES])
+def test_attention_sharp_softmax(name, over, lens, form, sigma):
+    w = _w(**over)
+    lens = np.asarray(lens, np.int32)
+    par = wl.trees(w, 9100 + len(name))
+    q, kc, vc, kt, vt = _inputs(w, lens, int(lens.max()) + 24, 9200 + len(name) + int(sigma), sigma, 0.5)
+    ref, err = _check(w, q, kc, vc, kt, vt, par, lens, form, f"{name} sigma={sigma}")
+    if sigma >= 2.0:
+        # scaled scores of spread 4: a few keys carry each row, so outputs are
+        # close to single V rows instead of the mean of many
+        assert np.abs(ref).mean() > 0.1, np.abs(ref).mean()
+    print(f"{name} sigma={sigma} form={form}: max-abs err {err:.2e}, mean|ref| {np.abs(ref).mean():.3f}")
+
+
+def _plant(kc, kt, q, b, g, col, tree_row, i, h, lam, wref):
+    """Set one key row of (b, g) to lam times query row (b, i, h): in the cache
+    at column `col`, or in the tree rows at `tree_row`."""
+    qv = gen.bf16_bits_to_f32(q[b, i, h]).astype(np.float32)
+    bits = gen.to_bf16_bits((lam * qv).astype(np.float32))
+    if tree_row is None:
+        kc[b, g, col] = bits
+    else:
+        kt[b, g, tree_row] = bits
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", ["gqa8-M40", "gqa4-M32"])
+def test_attention_planted_large_scores(form, shape):
+    if shape == "gqa8-M40":
+        w = _w(B=3, Hq=16, Hkv=2, D=128, M=40)
+        lens = np.array([5000, 2100, 3333], np.int32)
+    else:
+        w = _w(B=6, Hq=32, Hkv=8, D=128, M=32)
+        lens = np.array([4000, 1100, 7000, 2222, 64, 5555], np.int32)
+    par = wl.trees(w, 9300)
+    lmax = int(lens.max())
+    q, kc, vc, kt, vt = _inputs(w, lens, lmax + 16, 9301, w.qkv_sigma, w.qkv_sigma)
+    _, ost = oracle.validate(par, w.M)
+    omk, _ = oracle.mask(par, w.M, ost)
+    units = H.stream_units(w.B, w.T, w.Hq, w.Hkv, lens, H.cu_count())
+    rng = np.random.default_rng(9302)
+    lam = 400.0
+    slots = {}     # (b, g, "cache" | "tree", position) -> (i, h, where); a later plant replaces an earlier one
+    used = set()
+    for u in units:
+        def pick_row():
+            for _ in range(64):
+                r = int(rng.integers(u.row_lo, u.row_hi))
+                hl, i = divmod(r, w.T)
+                h = u.g * w.G + hl
+                if (u.b, i, h) not in used:
+                    used.add((u.b, i, h))
+                    return i, h
+            return None
+        L = int(lens[u.b])
+        # the first tile of every range that starts inside this unit's prefix
+        for x in u.cuts:
+            t = x - u.base
+            if t < u.n_prefix:
+                row = pick_row()
+                if row:
+                    slots[(u.b, u.g, "cache", lmax - L + min(L - 1, t * H.KT + 3 + u.qb))] = (*row, f"cut tile {t}")
+        # the last prefix tile, a tree row on the root path, the first prefix tile
+        if L > 0:
+            row = pick_row()
+            if row:
+                slots[(u.b, u.g, "cache", lmax - 1 - min(u.qb, L - 1))] = (*row, "last prefix column")
+            row = pick_row()
+            if row:
+                slots[(u.b, u.g, "cache", lmax - L + min(u.qb, L - 1))] = (*row, "first prefix column")
+        row = pick_row()
+        if row:
+            i, h = row
+            anc = [j for j in range(w.T) if (int(omk[u.b, i, j // 64]) >> (j % 64)) & 1]
+            slots[(u.b, u.g, "tree", anc[(len(anc) // 2 + u.qb) % len(anc)])] = (i, h, "tree row")
+    for (b, g, kind, pos), (i, h, _) in slots.items():
+        _plant(kc, kt, q, b, g, pos if kind == "cache" else None, pos if kind == "tree" else None, i, h, lam, w)
+    assert any("cut" in v[2] for v in slots.values())
+    ref, err = _check(w, q, kc, vc, kt, vt, par, lens, form, f"planted {shape}")
+    # the construction holds: a planted row puts all but a negligible weight on
+    # its planted key, so its output is that key's V row
+    f = lambda x: wl.as_f32(w, x)
+    for (b, g, kind, pos), (i, h, where) in slots.items():
+        v = f(vc[b, g, pos]) if kind == "cache" else f(vt[b, g, pos])
+        assert np.abs(ref[b, i, h] - v).max() < 1e-4, (b, i, h, where)
+    print(f"{shape} form={form}: {len(slots)} planted rows, max-abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+def test_attention_planted_increasing_maxima(form):
+    """One row whose maximum grows by 12 base-2 units in every prefix tile:
+    the running reference moves in every tile, and each piece of a cut unit
+    ends with a larger maximum than the one before; another row whose
+    maximum shrinks tile by tile (one rescale in the first tile, then none)."""
+    w = _w(B=2, Hq=8, Hkv=2, D=128, M=24)
+    lens = np.array([3000, 2900], np.int32)
+    par = wl.trees(w, 9400)
+    lmax = int(lens.max())
+    q, kc, vc, kt, vt = _inputs(w, lens, lmax + 8, 9401, w.qkv_sigma, w.qkv_sigma)
+    sc = 1.4426950408889634 / np.sqrt(w.D)
+    for (b, i, h, sign) in [(0, 5, 1, +1), (1, 17, 6, -1)]:
+        g = h // w.G
+        L = int(lens[b])
+        qv = gen.bf16_bits_to_f32(q[b, i, h]).astype(np.float64)
+        n2 = float(qv @ qv)
+        ntiles = (L + 63) // 64
+        for t in range(ntiles):
+            step = t if sign > 0 else ntiles - 1 - t
+            target = 4.0 + 12.0 * step          # base-2 score of the planted key
+            lam = target / (sc * n2)
+            col = lmax - L + min(L - 1, t * 64 + 11)
+            kc[b, g, col] = gen.to_bf16_bits((lam * qv).astype(np.float32))
+    _check(w, q, kc, vc, kt, vt, par, lens, form, "increasing maxima")
+
+
+# ------------------------------------------------------------------ argmax
+def _run_accept(logits, tokens, par, M):
+    B, T, V = logits.shape
+    i32 = lambda x: torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device=DEV)
+    lg = torch.as_tensor(logits, device=DEV)
+    tk, pr = i32(tokens), i32(par)
+    W = (T + 63) // 64
+    mk = torch.zeros(B, T, W, dtype=torch.int64, device=DEV)
+    dp = torch.zeros(B, T, dtype=torch.int32, device=DEV)
+    st = torch.zeros(B, dtype=torch.int32, device=DEV)
+    assert svt.svt_build_mask(pr, M, mk, dp, st) == 0
+    am = torch.full((B, T), -1, dtype=torch.int32, device=DEV)
+    al = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+    path = torch.full((B, T), -1, dtype=torch.int32, device=DEV)
+    bo = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+    args = svt.accept_args(lg, tk, pr, mk, dp, am, al, path, bo, status=st)
+    ws = torch.empty(svt.svt_accept_workspace(args), dtype=torch.uint8, device=DEV)
+    args = svt.accept_args(lg, tk, pr, mk, dp, am, al, path, bo, status=st, workspace=ws)
+    assert svt.svt_accept(args) == 0
+    torch.cuda.synchronize()
+    return H.from_dev(am), H.from_dev(al), H.from_dev(path), H.from_dev(bo)
+
+
+@pytest.mark.parametrize("V", [32000, 32003, 151552])
+def test_argmax_ties_and_nan_across_chunks(V):
+    B, M = 2, 16
+    T = M + 1
+    rows = B * T
+    nchunk, chunk = H.accept_chunking(rows, V)
+    assert nchunk >= 7, (nchunk, chunk)
+    x = np.round(gen.normal(gen.stream_key(9500, V), rows * V) * 2.0).astype(np.float32).reshape(rows, V)
+    c = lambda k, off=0: k * chunk + off          # index `off` inside chunk k
+    last = nchunk - 1
+    expect = {}
+    x[0, [c(0, 100), c(5, 7)]] = 50.0            # equal maxima in chunks 0 and 5
+    expect[0] = c(0, 100)
+    x[1, [c(1) - 1, c(1)]] = 50.0                 # tie across the boundary of chunks 0 / 1
+    expect[1] = c(1) - 1
+    x[2, [0, V - 1]] = 50.0                       # first and last entry (last chunk may be short)
+    expect[2] = 0
+    x[3, [c(3, 9), c(1, 2000)]] = np.nan          # NaN in two chunks: the lower index
+    expect[3] = c(1, 2000)
+    x[4] = -np.abs(x[4]) - 1.0                    # every value negative ...
+    x[4, c(6, 1)] = -0.0                          # ... but -0.0 in chunk 6
+    x[4, c(2, 5)] = 0.0                           # and +0.0 in chunk 2: equal, lower index
+    expect[4] = c(2, 5)
+    x[5] = -np.abs(x[5]) - 1.0
+    x[5, c(1, 3)] = -0.0                          # -0.0 first, +0.0 later: still the first
+    x[5, c(last, 0)] = 0.0
+    expect[5] = c(1, 3)
+    x[6] = -np.inf                                # all -inf: index 0
+    expect[6] = 0
+    x[7] = -np.inf
+    x[7, V - 1] = np.nan                          # NaN ranks above every number
+    expect[7] = V - 1
+    x[8, [c(4, 8), c(2, 64)]] = np.inf            # +inf in two chunks
+    expect[8] = c(2, 64)
+    x[9, V - 1] = 60.0                            # unique max at the very end
+    expect[9] = V - 1
+    x[10, [c(1), c(2) - 1]] = 50.0                # first and last entry of chunk 1
+    expect[10] = c(1)
+    x[11, [c(last, 0), c(last - 1, 3), c(2, 2)]] = 55.0   # three chunks, lowest wins
+    expect[11] = c(2, 2)
+    x[12, c(3, 1)] = np.nan                       # NaN beats +inf elsewhere
+    x[12, c(0, 1)] = np.inf
+    expect[12] = c(3, 1)
+    # rows 13..: quantised normals, ties at the top spread over many chunks
+    logits = x.reshape(B, T, V)
+    par = np.stack([gen.tree_depth_capped(gen.stream_key(9501, b), M, 10) for b in range(B)]).astype(np.int32)
+    am0 = oracle.argmax(logits)
+    for r, e in expect.items():
+        assert am0.reshape(-1)[r] == e, (r, am0.reshape(-1)[r], e)   # the oracle agrees with the construction
+    tok = np.zeros((B, T), np.int32)
+    for b in range(B):   # plant on the oracle's argmax so the paths run through the tied rows
+        for i in range(1, T):
+            tok[b, i] = am0[b, par[b, i]] if i % 5 else (am0[b, par[b, i]] + 1) % V
+    am, al, path, bo = _run_accept(logits, tok, par, M)
+    assert np.array_equal(am, am0)
+    _, ost = oracle.validate(par, M)
+    oal, opath, obo = oracle.accept(am0, tok, par, M, ost)
+    assert np.array_equal(al, oal) and np.array_equal(path, opath) and np.array_equal(bo, obo)

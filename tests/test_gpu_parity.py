@@ -306,30 +306,8 @@ def _attn_case(w, lens, cap, seed, parents=None, poison=True):
 
 
 def _run_attn(w, q, kc, vc, kt, vt, parents, lens, lmax_bound=None, status=None, scale=0.0, form=0):
-    lmax = int(lens.max()) if len(lens) else 0
-    B, T = parents.shape
-    M = T - 1
-    Wd = (T + 63) // 64
-    mk = torch.zeros(B, T, Wd, dtype=torch.int64, device=DEV)
-    dp = torch.zeros(B, T, dtype=torch.int32, device=DEV)
-    st = torch.zeros(B, dtype=torch.int32, device=DEV)
-    assert svt.svt_build_mask(_i32(parents), M, mk, dp, st) == 0
-    if status is not None:
-        st = _i32(status)
-    tq, tkc, tvc, tkt, tvt = (H.to_dev(x) for x in (q, kc, vc, kt, vt))
-    out = torch.full(tq.shape, float("nan"), dtype=tq.dtype, device=DEV)
-    sst = torch.full((B,), 55, dtype=torch.int32, device=DEV)
-    ln_t, lm_t = _i32(lens), _i32([lmax])
-    bound = lmax if lmax_bound is None else lmax_bound
-    args = svt.attn_args(tq, tkc, tvc, ln_t, lm_t, bound, tkt, tvt, mk, out, status=st, seq_status=sst,
-                         scale=scale, form=form)
-    need = svt.svt_verify_attention_workspace(args)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
-    args = svt.attn_args(tq, tkc, tvc, ln_t, lm_t, bound, tkt, tvt, mk, out, status=st, seq_status=sst,
-                         scale=scale, workspace=ws, form=form)
-    rc = svt.svt_verify_attention(args)
-    torch.cuda.synchronize()
-    return rc, out, H.from_dev(mk).view(np.uint64), H.from_dev(st), H.from_dev(sst)
+    return H.run_attention(q, kc, vc, kt, vt, parents, lens, lmax_bound=lmax_bound, status=status, scale=scale,
+                           form=form)
 
 
 def _small_w(base, **kw):

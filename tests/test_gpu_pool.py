@@ -216,8 +216,10 @@ def test_attention_seq_slot(form):
     torch.cuda.synchronize()
     assert (H.from_dev(sst) == 0).all()
     f = lambda x: wl.as_f32(w, x)
-    orc, ref = oracle.attention(f(q), f(kc), f(vc), f(kt), f(vt), H.from_dev(mk).view(np.uint64), lens, lmax,
-                                H.from_dev(st))
+    _, ost = oracle.validate(par, w.M)
+    omk, _ = oracle.mask(par, w.M, ost)
+    assert np.array_equal(H.from_dev(mk).view(np.uint64), omk) and np.array_equal(H.from_dev(st), ost)
+    orc, ref = oracle.attention(f(q), f(kc), f(vc), f(kt), f(vt), omk, lens, lmax, ost)
     H.check_attention(w, H.out_f32(w, out), ref, f"seq_slot form={form}")
     # a slot outside the pool (on the long sequence, which the split form cuts
     # into several key splits): it reports SVT_ERR_ARG and gets zeros; the

@@ -2,10 +2,10 @@
 configuration the benchmark uses.
 
 - mask, argmax and accept: every output, bit for bit;
-- attention (one layer): every row for the two small workloads, a seeded
-  sample of rows for the others, each recomputed by the oracle; plus
-  properties checked on every row (finite output although the padding holds
-  NaN, bitwise run-to-run determinism);
+- attention (one layer): every row of every workload, each recomputed by the
+  oracle from the oracle's own mask (the GPU's mask must equal it), plus
+  finite output although the padding holds NaN and bitwise run-to-run
+  determinism;
 - commit (all layers): a sample of (layer, KV head) slabs, plane K and V,
   against the oracle, plus tokens, position ids, lengths; columns beyond the
   new length untouched.
@@ -65,16 +65,6 @@ def test_workload_mask_and_accept(wi):
     print(f"[{w.name}] accept lengths {oal.tolist()[:8]} mean {oal.mean():.2f}", flush=True)
 
 
-def _sample_rows(w, n, seed):
-    """Seeded (b, node, head) triples, always including the root and last node."""
-    if w.B * w.T * w.Hq <= n:
-        return [(b, i, h) for b in range(w.B) for i in range(w.T) for h in range(w.Hq)]
-    r = gen.u64(gen.stream_key(seed, 4242), 3 * n)
-    rows = [(int(r[3 * k] % w.B), int(r[3 * k + 1] % w.T), int(r[3 * k + 2] % w.Hq)) for k in range(n)]
-    rows += [(0, 0, 0), (w.B - 1, w.T - 1, w.Hq - 1)]
-    return rows
-
-
 @pytest.mark.parametrize("wi", WIDS, ids=[w.name for w in wl.WORKLOADS])
 def test_workload_attention(wi):
     w = wl.workload(wi)
@@ -85,6 +75,10 @@ def test_workload_attention(wi):
     cap = lmax + 64
     q, kc, vc, kt, vt = wl.attention_inputs(w, lens, cap)      # padding columns hold NaN
     mk, dp, st = _mask_on_gpu(w, parents)
+    # the oracle's own mask and status (the GPU's must equal them)
+    _, ost = oracle.validate(parents, w.M)
+    omk, _ = oracle.mask(parents, w.M, ost)
+    assert np.array_equal(H.from_dev(mk).view(np.uint64), omk) and np.array_equal(H.from_dev(st), ost)
     tq, tkc, tvc, tkt, tvt = (H.to_dev(x) for x in (q, kc, vc, kt, vt))
     out = torch.full(tq.shape, float("nan"), dtype=tq.dtype, device=DEV)
     sst = torch.full((w.B,), 55, dtype=torch.int32, device=DEV)
@@ -102,18 +96,17 @@ def test_workload_attention(wi):
     assert (H.from_dev(sst) == 0).all()
     got = H.out_f32(w, out)
     assert np.isfinite(got).all(), "NaN padding leaked into the output"
-    omk = H.from_dev(mk).view(np.uint64)
-    rows = _sample_rows(w, 192, w.seed)
-    print(f"[{w.name}] oracle on {len(rows)} rows", flush=True)
-    f = lambda x: wl.as_f32(w, x)
-    ref = np.zeros((len(rows), w.D))
-    sel = np.zeros((len(rows), w.D), np.float32)
-    scale = 1.0 / np.sqrt(w.D)
-    for k, (b, i, h) in enumerate(rows):
-        g = h // w.G
-        ref[k] = oracle.attention_row(f(q[b, i, h]), f(kc[b, g]), f(vc[b, g]), f(kt[b, g]), f(vt[b, g]), omk[b, i],
-                                      int(lens[b]), lmax, scale)
-        sel[k] = got[b, i, h]
+    del tq, tkc, tvc, tkt, tvt
+    # every row, each recomputed by the oracle (rows run side by side on the
+    # host's cores); with the stream form this includes every row of the
+    # units that range ends cut, which go through the partial merge
+    rows = [(b, i, h) for b in range(w.B) for i in range(w.T) for h in range(w.Hq)]
+    if w.dtype == "bf16" and w.B <= 1024:
+        units = H.stream_units(w.B, w.T, w.Hq, w.Hkv, lens, H.cu_count())
+        print(f"[{w.name}] {sum(1 for u in units if u.cuts)} of {len(units)} stream units are cut", flush=True)
+    print(f"[{w.name}] oracle on all {len(rows)} rows, {oracle.default_threads()} threads", flush=True)
+    ref = oracle.attention_rows(q, kc, vc, kt, vt, omk, lens, lmax, rows, to_f32=lambda x: wl.as_f32(w, x))
+    sel = got.reshape(-1, w.D)     # rows in (b, i, h) order
     err = H.check_attention(w, sel, ref, w.name)
     print(f"[{w.name}] max-abs error {err:.3e} over {len(rows)} rows", flush=True)
 

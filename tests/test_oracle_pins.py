@@ -285,6 +285,27 @@ def test_attention_batch_equals_alone():
         assert np.array_equal(o1[0], out[b])
 
 
+def test_attention_rows_threads_equal_serial():
+    """The threaded row driver returns exactly the serial driver's rows (the
+    same C routine per row, in any thread order), for any thread count and
+    with a bf16-style converter applied slab by slab."""
+    c = _attn_case(3, 20, 8, 2, 64, [50, 0, 130], 140, 21)
+    _, out = oracle.attention(c["q"], c["kc"], c["vc"], c["kt"], c["vt"], c["mk"], c["lens"], c["lmax"])
+    rows = [(b, i, h) for b in range(3) for i in range(21) for h in range(8)][::3]
+    want = np.stack([out[b, i, h] for b, i, h in rows])
+    for th in (1, 4, 7):
+        got = oracle.attention_rows(c["q"], c["kc"], c["vc"], c["kt"], c["vt"], c["mk"], c["lens"], c["lmax"],
+                                    rows, threads=th)
+        assert np.array_equal(got, want), th
+    bits = lambda x: gen.to_bf16_bits(np.asarray(x, np.float32))
+    up = gen.bf16_bits_to_f32
+    _, out16 = oracle.attention(up(bits(c["q"])), up(bits(c["kc"])), up(bits(c["vc"])), up(bits(c["kt"])),
+                                up(bits(c["vt"])), c["mk"], c["lens"], c["lmax"])
+    got16 = oracle.attention_rows(bits(c["q"]), bits(c["kc"]), bits(c["vc"]), bits(c["kt"]), bits(c["vt"]),
+                                  c["mk"], c["lens"], c["lmax"], rows, threads=5, to_f32=up)
+    assert np.array_equal(got16, np.stack([out16[b, i, h] for b, i, h in rows]))
+
+
 def test_attention_closed_forms():
     B, M, Hq, Hkv, D = 2, 7, 4, 1, 8
     c = _attn_case(B, M, Hq, Hkv, D, [5, 2], 6, 29)
