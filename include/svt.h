@@ -24,7 +24,8 @@
  *   - Pointers are device memory owned by the caller unless the name ends in
  *     _host.  The library keeps no state between calls.  Calls that need
  *     scratch memory take a caller-provided workspace whose size a *_workspace
- *     query returns; the library itself allocates nothing.
+ *     query returns; the library itself allocates nothing.  The one exception,
+ *     svt_accept_noalloc, uses a fixed static device buffer instead.
  *   - Every call enqueues its kernels on the caller's stream and returns at once,
  *     except where SVT_SYNC_CHECK is given (then it synchronises that stream).
  *   - The return value is SVT_OK or a negative svt_status.  Argument errors are
@@ -217,6 +218,21 @@ typedef struct svt_accept_args {
  * for the batch size being run, or for the largest need over the sizes used. */
 size_t svt_accept_workspace(const svt_accept_args* a);
 int svt_accept(const svt_accept_args* a, hipStream_t stream);
+
+/* svt_accept_noalloc: svt_accept for callers that cannot allocate device     */
+/* memory (code under HIP graph capture, tight serving loops, harnesses that  */
+/* forbid hipMalloc).  Same arguments, outputs and errors as svt_accept,      */
+/* except that a->workspace and a->workspace_bytes are ignored: the chunk     */
+/* keys go to a static device buffer of SVT_ACCEPT_NOALLOC_SCRATCH bytes that  */
+/* the library holds on each GPU it runs on until the process ends.  A shape  */
+/* whose svt_accept_workspace exceeds that returns SVT_ERR_WORKSPACE before    */
+/* anything is launched.  The call allocates nothing and calls no allocating  */
+/* routine.  Every call on one GPU shares that GPU's buffer (it keeps the last */
+/* call's contents, none of which a later call reads): calls that overlap on  */
+/* one GPU (different streams, or different threads on one stream without     */
+/* ordering) race and must not be issued.                                      */
+#define SVT_ACCEPT_NOALLOC_SCRATCH (4u << 20)
+int svt_accept_noalloc(const svt_accept_args* a, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* svt_commit                                                                */

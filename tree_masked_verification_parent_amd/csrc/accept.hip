@@ -19,9 +19,38 @@
 // keys of each node, forms the ok bits with one ballot per 64 nodes, tests
 // every node's ancestor mask against them, and picks the deepest accepted node
 // (lowest index on ties) with a wave max over (depth+1) << 16 | (0xFFFF - i).
+#include <mutex>
+
 #include "svt_internal.h"
 
 namespace svt {
+
+// Scratch of svt_accept_noalloc: the chunk keys live in this file-scope
+// device array instead of a caller workspace.  Each device the library runs
+// on holds its own copy for the life of the process.  In host code the name
+// `scratch` is only a host-side handle; the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is handed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[kAcceptScratchBytes];
+
+hipError_t accept_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 __device__ __forceinline__ uint32_t order_bits(float x) {
   uint32_t u = __float_as_uint(x);

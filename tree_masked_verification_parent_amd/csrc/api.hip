@@ -100,22 +100,51 @@ size_t svt_accept_workspace(const svt_accept_args* a) {
   return p.ws_bytes;
 }
 
+// Host checks shared by svt_accept and svt_accept_noalloc (everything but the
+// workspace); SVT_OK with *p filled, or the status to return.
+static int accept_checks(const svt_accept_args* a, svt::AcceptPlan* p) {
+  if (a->B < 0 || a->M < 0 || a->V <= 0) return SVT_ERR_ARG;
+  if (a->M >= SVT_MAX_T) return SVT_ERR_UNSUPPORTED;
+  if (a->B == 0) return SVT_OK;
+  if (!a->logits || !a->tree_tokens || !a->parents || !a->mask || !a->depth || !a->amax || !a->accept_len ||
+      !a->path || !a->bonus || !aligned(a->mask, 8) || !aligned(a->logits, 4))
+    return SVT_ERR_ARG;
+  if (!svt::plan_accept(a, p)) return SVT_ERR_ARG;
+  if ((int64_t)p->rows * p->nchunk > 0x7FFFFFFF) return SVT_ERR_UNSUPPORTED;
+  return SVT_OK;
+}
+
 int svt_accept(const svt_accept_args* a, hipStream_t stream) {
   char shape[96];
   if (!a) return finish("svt_accept", SVT_ERR_ARG, "null args");
   std::snprintf(shape, sizeof shape, "B=%d M=%d V=%d", a->B, a->M, a->V);
-  if (a->B < 0 || a->M < 0 || a->V <= 0) return finish("svt_accept", SVT_ERR_ARG, shape);
-  if (a->M >= SVT_MAX_T) return finish("svt_accept", SVT_ERR_UNSUPPORTED, shape);
-  if (a->B == 0) return finish("svt_accept", SVT_OK, shape);
-  if (!a->logits || !a->tree_tokens || !a->parents || !a->mask || !a->depth || !a->amax || !a->accept_len ||
-      !a->path || !a->bonus || !aligned(a->mask, 8) || !aligned(a->logits, 4))
-    return finish("svt_accept", SVT_ERR_ARG, shape);
   svt::AcceptPlan p;
-  if (!svt::plan_accept(a, &p)) return finish("svt_accept", SVT_ERR_ARG, shape);
-  if ((int64_t)p.rows * p.nchunk > 0x7FFFFFFF) return finish("svt_accept", SVT_ERR_UNSUPPORTED, shape);
+  const int rc = accept_checks(a, &p);
+  if (rc != SVT_OK || a->B == 0) return finish("svt_accept", rc, shape);
   if (!a->workspace || a->workspace_bytes < p.ws_bytes || !aligned(a->workspace, 8))
     return finish("svt_accept", SVT_ERR_WORKSPACE, shape);
   return finish("svt_accept", hip_rc(svt::launch_accept(a, p, stream)), shape);
+}
+
+int svt_accept_noalloc(const svt_accept_args* a, hipStream_t stream) {
+  char shape[96];
+  if (!a) return finish("svt_accept_noalloc", SVT_ERR_ARG, "null args");
+  std::snprintf(shape, sizeof shape, "B=%d M=%d V=%d", a->B, a->M, a->V);
+  svt::AcceptPlan p;
+  const int rc = accept_checks(a, &p);
+  if (rc != SVT_OK || a->B == 0) return finish("svt_accept_noalloc", rc, shape);
+  if (p.ws_bytes > svt::kAcceptScratchBytes) {
+    if (trace_on())
+      std::fprintf(stderr, "[svt] svt_accept_noalloc needs %zu scratch bytes, the static buffer holds %zu\n",
+                   p.ws_bytes, svt::kAcceptScratchBytes);
+    return finish("svt_accept_noalloc", SVT_ERR_WORKSPACE, shape);
+  }
+  void* ws = nullptr;  // device address of the static scratch on the current device
+  if (svt::accept_scratch(&ws) != hipSuccess || !ws) return finish("svt_accept_noalloc", SVT_ERR_HIP, shape);
+  svt_accept_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = svt::kAcceptScratchBytes;
+  return finish("svt_accept_noalloc", hip_rc(svt::launch_accept(&b, p, stream)), shape);
 }
 
 static int commit_impl(const char* name, const svt_commit_args* a, bool by_length, int32_t flags,

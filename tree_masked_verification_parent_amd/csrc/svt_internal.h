@@ -39,6 +39,11 @@ struct AcceptPlan {
 };
 bool plan_accept(const svt_accept_args* a, AcceptPlan* p);
 
+// Static device scratch of svt_accept_noalloc (accept.hip): its size, and its
+// device address on the current device (resolved once per device).
+constexpr size_t kAcceptScratchBytes = SVT_ACCEPT_NOALLOC_SCRATCH;
+hipError_t accept_scratch(void** out);
+
 // ---- launchers (defined next to their kernels); return hipError_t ----
 hipError_t launch_build_mask(const int32_t* parents, int B, int M, uint64_t* mask, int32_t* depth,
                              int32_t* status, hipStream_t s);

@@ -68,8 +68,8 @@ class RealignArgs(ctypes.Structure):
 
 
 EXPORTS = ["svt_build_mask", "svt_expand_mask", "svt_verify_attention_workspace", "svt_verify_attention",
-           "svt_accept_workspace", "svt_accept", "svt_commit", "svt_commit_length", "svt_realign", "svt_pool_pick",
-           "svt_check_status", "svt_status_string", "svt_version"]
+           "svt_accept_workspace", "svt_accept", "svt_accept_noalloc", "svt_commit", "svt_commit_length",
+           "svt_realign", "svt_pool_pick", "svt_check_status", "svt_status_string", "svt_version"]
 
 _lib = None
 
@@ -92,6 +92,8 @@ def lib():
         L.svt_accept_workspace.restype = ctypes.c_size_t
         L.svt_accept.argtypes = [ctypes.POINTER(AcceptArgs), _P]
         L.svt_accept.restype = ctypes.c_int
+        L.svt_accept_noalloc.argtypes = [ctypes.POINTER(AcceptArgs), _P]
+        L.svt_accept_noalloc.restype = ctypes.c_int
         L.svt_commit.argtypes = [ctypes.POINTER(CommitArgs), _I32, _P]
         L.svt_commit.restype = ctypes.c_int
         L.svt_commit_length.argtypes = [ctypes.POINTER(CommitArgs), _I32, _P]
@@ -215,6 +217,14 @@ def svt_accept_workspace(args: AcceptArgs) -> int:
 
 def svt_accept(args: AcceptArgs, stream=None) -> int:
     return lib().svt_accept(ctypes.byref(args), _stream(stream))
+
+
+SVT_ACCEPT_NOALLOC_SCRATCH = 4 << 20
+
+
+def svt_accept_noalloc(args: AcceptArgs, stream=None) -> int:
+    """svt_accept with the library's static scratch (args.workspace ignored)."""
+    return lib().svt_accept_noalloc(ctypes.byref(args), _stream(stream))
 
 
 def commit_args(kv_main, kv_branch, lens, lmax, path, accept_len, commit_status, tokens_main=None,
