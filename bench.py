@@ -191,14 +191,32 @@ def algorithmic_bytes_accept(w):
     return w.B * w.T * w.V * 4
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, parents, lens, logits, tokens, seed, budget_s):
-    """Time the oracle (single-threaded C, double precision) on a bounded
-    sample of the same workload and scale it to one full step."""
+    """Time the oracle (plain C, double precision, unchanged) on a bounded
+    sample of the same workload and scale it to one full step, twice: on one
+    thread, and with the sampled attention rows and commit slabs spread over
+    the host's cores (oracle.attention_rows: the same C row routine, rows run
+    side by side; commit slabs as independent oracle calls side by side).
+    Mask and accept are single-threaded in both legs (they are a small part)."""
+    import concurrent.futures as cf
+
     import oracle
     from synth import gen
     from synth import workloads as wl
 
     t_all = time.perf_counter()
+    nthreads = oracle.default_threads()
     lmax = int(lens.max())
     # mask + validate: whole batch
     t0 = time.perf_counter()
@@ -211,27 +229,37 @@ def cpu_baseline(w, parents, lens, logits, tokens, seed, budget_s):
     al, path, _ = oracle.accept(am, tokens, parents, w.M, st)
     t_accept = time.perf_counter() - t0
     # attention: whole sequences of one layer, in a seeded order, until the
-    # sample (inputs included) has used about 80 % of the budget
+    # one-thread sample has used about 60 % of the budget; then the same
+    # sequences again with their rows over `nthreads` threads
     order = np.argsort(gen.u64(gen.stream_key(seed, 991), w.B))
-    picked, t_attn_sample, keys_sample = [], 0.0, 0
+    picked, t_attn_sample, keys_sample, inputs = [], 0.0, 0, []
     t_part = time.perf_counter()
     sub = wl.Workload(**{**w.__dict__, "B": 1})
+    f = lambda x: wl.as_f32(sub, x)
     for b in order:
-        if picked and time.perf_counter() - t_part > 0.8 * budget_s:
+        if picked and time.perf_counter() - t_part > 0.6 * budget_s:
             break
         Lb = int(lens[b])
         q, kc, vc, kt, vt = wl.attention_inputs(sub, np.array([Lb], np.int32), Lb, seed + 1000 + int(b),
                                                 poison=False)
-        f = lambda x: wl.as_f32(sub, x)
         args = (f(q), f(kc), f(vc), f(kt), f(vt), mk[b:b + 1], np.array([Lb], np.int32), Lb)
         t0 = time.perf_counter()
         oracle.attention(*args)
         t_attn_sample += time.perf_counter() - t0
         keys_sample += Lb
         picked.append(int(b))
+        inputs.append(args)
+    t0 = time.perf_counter()
+    rows = [(0, i, h) for i in range(w.T) for h in range(w.Hq)]
+    for args in inputs:
+        oracle.attention_rows(*args[:7], args[7], rows, threads=nthreads)
+    t_attn_sample_mt = time.perf_counter() - t0
+    del inputs
     t_attn_layer = t_attn_sample * float(lens.sum()) / max(keys_sample, 1)
-    # commit: one layer, one KV head (every layer, plane and head moves the
-    # same way); the bytes moved do not depend on their values
+    t_attn_layer_mt = t_attn_sample_mt * float(lens.sum()) / max(keys_sample, 1)
+    # commit: one layer and one KV head per oracle call (every layer, plane
+    # and head moves the same way; the bytes moved do not depend on their
+    # values); nthreads such calls side by side for the threaded leg
     T = w.T
     cap = lmax + T + 8
     row_el = w.D * w.esize // 2
@@ -242,20 +270,34 @@ def cpu_baseline(w, parents, lens, logits, tokens, seed, budget_s):
     t0 = time.perf_counter()
     oracle.commit(km, kb, w.M, tm, tokens, lens, lmax, path, al, st)
     t_commit_slab = time.perf_counter() - t0
-    t_commit = t_commit_slab * w.layers * w.Hkv
+    n_slabs = w.layers * w.Hkv
+    t_commit = t_commit_slab * n_slabs
+    par_calls = min(nthreads, n_slabs)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=par_calls) as ex:
+        list(ex.map(lambda _: oracle.commit(km, kb, w.M, tm, tokens, lens, lmax, path, al, st), range(par_calls)))
+    t_commit_mt = (time.perf_counter() - t0) * -(-n_slabs // par_calls)
     step_s = t_mask + w.layers * t_attn_layer + t_accept + t_commit
+    step_s_mt = t_mask + w.layers * t_attn_layer_mt + t_accept + t_commit_mt
+    sample = (f"oracle (fp64 C, unchanged) on the same workload: mask+accept for all {w.B} sequences "
+              f"(1 thread); one-layer attention for sequences {picked} ({keys_sample} of {int(lens.sum())} "
+              f"prefix keys), scaled by keys and by {w.layers} layers; commit of one layer and one KV head per "
+              f"call, scaled by {w.layers} layers x {w.Hkv} heads; {time.perf_counter() - t_all:.1f} s wall")
+    one = {"value": w.B * w.M / step_s, "cores": 1, "est_step_s": step_s,
+           "est_parts_s": {"mask": t_mask, "attention_per_layer": t_attn_layer, "accept": t_accept,
+                           "commit": t_commit}}
     return {
-        "value": w.B * w.M / step_s,
+        "value": w.B * w.M / step_s_mt,
         "unit": "verified tree nodes/s",
-        "cores": 1,
+        "cores": nthreads,
         "kind": "oracle",
-        "sample": (f"oracle (1 thread, fp64) on the same workload: mask+accept for all {w.B} sequences; "
-                   f"one-layer attention for sequences {picked} ({keys_sample} of {int(lens.sum())} prefix "
-                   f"keys), scaled by keys and by {w.layers} layers; commit of one layer and one KV head, "
-                   f"scaled by {w.layers} layers x {w.Hkv} heads; {time.perf_counter() - t_all:.1f} s wall"),
-        "est_step_s": step_s,
-        "est_parts_s": {"mask": t_mask, "attention_per_layer": t_attn_layer, "accept": t_accept,
-                        "commit": t_commit},
+        "sample": sample + f"; attention rows and commit calls over {nthreads} threads",
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "est_step_s": step_s_mt,
+        "est_parts_s": {"mask": t_mask, "attention_per_layer": t_attn_layer_mt, "accept": t_accept,
+                        "commit": t_commit_mt},
+        "single_thread": one,
     }
 
 
@@ -736,14 +778,27 @@ def main():
     assert rc == 0 and r.commit_status.item() == 0
     assert np.array_equal(r.len.cpu().numpy(), lens0 + A)
 
-    def dur(i, j):
-        return float(np.mean([evs[k][i].elapsed_time(evs[k][j]) for k in range(args.steps)])) * 1e-3
+    def per_step(i, j, div=1):
+        return np.array([evs[k][i].elapsed_time(evs[k][j]) for k in range(args.steps)]) * 1e-3 / div
+
+    def dur(i, j, div=1):
+        return float(np.mean(per_step(i, j, div)))
+
+    def dist_us(i, j, div=1):
+        x = per_step(i, j, div) * 1e6
+        return {"mean": float(x.mean()), "p10": float(np.percentile(x, 10)), "p50": float(np.median(x)),
+                "p90": float(np.percentile(x, 90)), "min": float(x.min()), "max": float(x.max())}
 
     t_mask = dur(0, 1)
-    t_attn = dur(1, 2) / L
+    t_attn = dur(1, 2, L)
     t_accept = dur(2, 3)
     t_commit = dur(3, 4)
     ms_per_step = elapsed / args.steps * 1e3
+    # distribution over the timed steps of each call type (attention: the
+    # step's mean per layer) and of the whole step between its first and
+    # last event
+    timing = {"steps": args.steps, "mask_us": dist_us(0, 1), "attention_us_per_layer": dist_us(1, 2, L),
+              "accept_us": dist_us(2, 3), "commit_us": dist_us(3, 4), "step_us": dist_us(0, 4)}
 
     attn_bytes = algorithmic_bytes_attention(w, lens0, w.T)
     attn_flops = flops_attention(w, lens0, depth)
@@ -802,6 +857,7 @@ def main():
         "accept_us": t_accept * 1e6,
         "mask_us": t_mask * 1e6,
         "verified_nodes_per_s_one_layer": w.B * w.M / (t_mask + t_attn + t_accept),
+        "timing": timing,
         "dominant": dominant,
         "roofline": roof(dominant),
         "roofline_attention": roof("attention"),

@@ -30,12 +30,15 @@ def test_cpu_baseline_leg_on_the_smallest_workload():
     lens = wl.lengths(w, w.seed)
     logits, tokens, _ = wl.logits_and_drafts(w, parents, w.seed)
     cb = bench.cpu_baseline(w, parents, lens, logits, tokens, w.seed, 0.5)
-    assert cb["kind"] == "oracle" and cb["cores"] == 1
-    assert cb["unit"] == "verified tree nodes/s"
-    assert np.isfinite(cb["value"]) and cb["value"] > 0
-    parts = cb["est_parts_s"]
-    step = parts["mask"] + w.layers * parts["attention_per_layer"] + parts["accept"] + parts["commit"]
-    assert cb["value"] == pytest.approx(w.B * w.M / step)
+    import oracle
+    assert cb["kind"] == "oracle" and cb["cores"] == oracle.default_threads()
+    assert cb["single_thread"]["cores"] == 1
+    assert cb["unit"] == "verified tree nodes/s" and cb["cpu_model"]
+    for leg in (cb, cb["single_thread"]):
+        assert np.isfinite(leg["value"]) and leg["value"] > 0
+        parts = leg["est_parts_s"]
+        step = parts["mask"] + w.layers * parts["attention_per_layer"] + parts["accept"] + parts["commit"]
+        assert leg["value"] == pytest.approx(w.B * w.M / step)
     assert str(int(lens.sum())) in cb["sample"]
 
 
@@ -63,6 +66,10 @@ def test_bench_prints_one_json_line_with_the_contract_fields():
             assert f in roof
     ra = d["roofline_attention"]
     assert ra["frac"] == pytest.approx(ra["achieved"] / ra["peak"])
+    t = d["timing"]
+    for k in ("mask_us", "attention_us_per_layer", "accept_us", "commit_us", "step_us"):
+        assert t[k]["p10"] <= t[k]["p50"] <= t[k]["p90"] and t[k]["p50"] > 0, k
+    assert t["attention_us_per_layer"]["mean"] == pytest.approx(d["attn_us_per_layer"])
     assert d["copy_GBps"] > 0
     cold = d["attention_cold"]
     assert cold["copies"] >= 2 and cold["us_per_call"] > 0
