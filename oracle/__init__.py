@@ -14,17 +14,28 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "svt_oracle.c")
-_LIB = os.path.join(_HERE, "libsvt_oracle.so")
+# SVT_SANITIZE=1 selects an AddressSanitizer + UBSan build (clang's runtime,
+# which the process must preload), kept apart from the normal library.
+SANITIZE = os.environ.get("SVT_SANITIZE", "0") not in ("", "0")
+_LIB = os.path.join(_HERE, "libsvt_oracle_san.so" if SANITIZE else "libsvt_oracle.so")
+CLANG = "/opt/rocm/llvm/bin/clang"
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g",
+             "-shared-libasan"]
 
 OK, ERR_ARG, ERR_TREE_ROOT, ERR_TREE_RANGE, ERR_TREE_CYCLE, ERR_CAPACITY, ERR_LENGTH = 0, -1, -3, -4, -5, -6, -9
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (ISO C11: no FMA contraction, no fast-math)."""
+    """Compile the oracle with gcc (ISO C11: no FMA contraction, no fast-math),
+    or with clang and AddressSanitizer + UBSan when SVT_SANITIZE=1."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-                               _SRC, "-lm", "-o", tmp])
+        if SANITIZE:
+            cmd = [CLANG, "-O1", "-std=c11", "-Wall", "-Wextra", *SAN_FLAGS, "-shared", "-fPIC", _SRC, "-lm",
+                   "-o", tmp]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-lm", "-o", tmp]
+        subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB
 

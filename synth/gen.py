@@ -17,15 +17,25 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fastgen.c")
-_LIB = os.path.join(_HERE, "libsynth.so")
+# SVT_SANITIZE=1 selects an AddressSanitizer + UBSan build (clang's runtime,
+# which the process must preload), kept apart from the normal library.
+SANITIZE = os.environ.get("SVT_SANITIZE", "0") not in ("", "0")
+_LIB = os.path.join(_HERE, "libsynth_san.so" if SANITIZE else "libsynth.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the C generator core with gcc (ISO C11, no fast-math)."""
+    """Compile the C generator core with gcc (ISO C11, no fast-math), or with
+    clang and AddressSanitizer + UBSan when SVT_SANITIZE=1."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", _SRC, "-lm", "-o", tmp])
+        if SANITIZE:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-std=c11", "-fsanitize=address,undefined",
+                   "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g", "-shared-libasan", "-shared",
+                   "-fPIC", _SRC, "-lm", "-o", tmp]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", _SRC, "-lm", "-o", tmp]
+        subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB
 

@@ -15,7 +15,10 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsvt.so")
+# SVT_SANITIZE=1 loads the build whose host code carries AddressSanitizer and
+# UBSan (see build.py); the device code is the same.
+LIB_PATH = os.path.join(_HERE, "libsvt_san.so" if os.environ.get("SVT_SANITIZE", "0") not in ("", "0")
+                        else "libsvt.so")
 
 SVT_OK = 0
 SVT_ERR_ARG = -1
