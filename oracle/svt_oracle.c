@@ -271,6 +271,17 @@ void oracle_accept(const int32_t* amax, const int32_t* tree_tokens, const int32_
 /* ------------------------------------------------------------------------ */
 static int slot_of(const int32_t* slot, int32_t b) { return slot ? slot[b] : b; }
 
+/* Reading ([BSD] §2, SequencePool: every pool sequence keeps its own cache
+ * row): a batch names each pool row at most once.  1 if two sequences share
+ * a slot. */
+static int slots_repeat(const int32_t* slot, int32_t B) {
+  if (!slot) return 0;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t c = 0; c < b; ++c)
+      if (slot[c] == slot[b]) return 1;
+  return 0;
+}
+
 /* Branch row of accepted step k of sequence b: the path entry, or k itself
  * for the length-based commit of [EP-nl] §2.A (no path given). */
 static int32_t step_row(const int32_t* path, int32_t T, int32_t b, int32_t k) {
@@ -311,6 +322,7 @@ int oracle_commit(uint8_t* kv_main, const uint8_t* kv_branch, int32_t n_layers, 
     int32_t new_end = mode == 1 ? old_lmax + A[b] : len[b] + A[b];
     if (new_end > new_lmax) new_lmax = new_end;
   }
+  if (slots_repeat(slot, B)) arg_bad = 1;
   if (arg_bad) { free(A); free(start); return ORACLE_ERR_ARG; }
   if ((int64_t)new_lmax > cap) { free(A); free(start); return ORACLE_ERR_CAPACITY; }
   /* New start column of each sequence's content. */
@@ -380,6 +392,7 @@ int oracle_realign(uint8_t* kv_main, int32_t n_layers, int32_t B, int32_t Hkv, i
   }
   for (int32_t b = 0; b < B; ++b)
     if (slot_of(slot, b) < 0 || slot_of(slot, b) >= rows) return ORACLE_ERR_ARG;
+  if (slots_repeat(slot, B)) return ORACLE_ERR_ARG;
   uint8_t* tmp = (uint8_t*)malloc((size_t)(E > 0 ? E : 1) * (size_t)row_bytes);
   for (int32_t l = 0; l < n_layers; ++l)
     for (int32_t kv = 0; kv < 2; ++kv)

@@ -121,6 +121,8 @@ def test_commit_slot_and_capacity_errors_write_nothing():
     kb, tok, al, path = _round_inputs(B, Hkv, L, M, D, 2, 16)
     for mode, slot, acc, want in [(svt.SVT_COMMIT_APPEND, [0, 4, 1], al, oracle.ERR_ARG),
                                   (svt.SVT_COMMIT_REPAD, [0, -1, 1], al, oracle.ERR_ARG),
+                                  (svt.SVT_COMMIT_REPAD, [1, 3, 1], al, oracle.ERR_ARG),     # row 1 twice
+                                  (svt.SVT_COMMIT_APPEND, [2, 2, 0], al, oracle.ERR_ARG),    # row 2 twice
                                   (svt.SVT_COMMIT_APPEND, [0, 2, 1], np.array([0, 4, 0], np.int32),
                                    oracle.ERR_CAPACITY)]:
         slot = np.array(slot, np.int32)
@@ -136,6 +138,31 @@ def test_commit_slot_and_capacity_errors_write_nothing():
     assert svt.svt_commit(args) == svt.SVT_ERR_ARG
     args.mode, args.n_slots = 0, 0
     assert svt.svt_commit(args) == svt.SVT_ERR_ARG
+
+
+def test_commit_slots_with_equal_residue_are_distinct():
+    """The device's duplicate check hashes slots into a 32768-bit table; slots
+    that share a bit but differ are accepted, a slot named twice is not."""
+    B, Hkv, L, M, D, cap = 3, 1, 1, 6, 64, 16
+    rows = 32768 + 8
+    km, tm = _pool(rows, Hkv, L, D, cap, 2, 23)
+    kb, tok, al, path = _round_inputs(B, Hkv, L, M, D, 2, 24)
+    lens = np.array([5, 0, 3], np.int32)
+    for slot, want in [([5, 5 + 32768, 7], 0), ([5, 5 + 32768, 5 + 32768], oracle.ERR_ARG)]:
+        slot = np.array(slot, np.int32)
+        print(f"commit slots {slot.tolist()}", flush=True)
+        rc, gkm, gtm, gln, glm, gpos, gcst = _run_commit(km, kb, tm, tok, lens, 5, path, al, D, 2,
+                                                         svt.SVT_COMMIT_REPAD, slot)
+        orc, okm, otm, oln, olm, opos = oracle.commit(km, kb, M, tm, tok, lens, 5, path, al, slot=slot)
+        assert rc == 0 and gcst == orc == want
+        if want:
+            assert np.array_equal(gkm, km) and np.array_equal(gtm, tm) and (gpos == -3).all()
+            continue
+        assert np.array_equal(gln, oln) and glm == olm
+        for b, r in enumerate(slot):
+            s0 = olm - oln[b]
+            assert np.array_equal(gkm[:, :, r, :, s0:olm], okm[:, :, r, :, s0:olm])
+            assert np.array_equal(gtm[r, s0:olm], otm[r, s0:olm]) and np.array_equal(gpos[r, :olm], opos[r, :olm])
 
 
 def _run_realign(km, tm, lens, ends, D, esize, slot=None):
@@ -176,7 +203,7 @@ def test_realign_errors_write_nothing():
     km, tm = _pool(rows, Hkv, L, D, cap, 2, 19)
     lens = np.array([5, 9, 2], np.int32)
     for ends, slot, want in [([5, 41, 3], None, oracle.ERR_LENGTH), ([4, 20, 3], None, oracle.ERR_LENGTH),
-                             ([5, 20, 3], [0, 3, 1], oracle.ERR_ARG)]:
+                             ([5, 20, 3], [0, 3, 1], oracle.ERR_ARG), ([5, 20, 3], [2, 0, 2], oracle.ERR_ARG)]:
         sl = None if slot is None else np.array(slot, np.int32)
         rc, gkm, gtm, glm, gpos, grs = _run_realign(km, tm, lens, np.array(ends, np.int32), D, 2, sl)
         orc = oracle.realign(km, lens, ends, tokens_main=tm, slot=sl)[0]

@@ -147,6 +147,12 @@ def test_slot_map_equals_gather_scatter(mode):
     bad = np.array([4, 6, 2], np.int32)
     rc, km3, *_ = oracle.commit(km, kb, M, tm, tok, lens, lmax, path, al, mode=mode, slot=bad)
     assert rc == oracle.ERR_ARG and np.array_equal(km3, km)
+    # a pool row named by two sequences of the batch: refused, nothing written
+    for dup in ([4, 0, 4], [2, 2, 0]):
+        rc, km4, tm4, ln4, lm4, _ = oracle.commit(km, kb, M, tm, tok, lens, lmax, path, al, mode=mode,
+                                                  slot=np.array(dup, np.int32))
+        assert rc == oracle.ERR_ARG and np.array_equal(km4, km) and np.array_equal(tm4, tm)
+        assert np.array_equal(ln4, lens) and lm4 == lmax
 
 
 def test_realign_identity_rectangle_and_slots():
@@ -169,5 +175,7 @@ def test_realign_identity_rectangle_and_slots():
     assert np.array_equal(k2[:, :, 2], km[:, :, 2])                         # row not in the batch
     rc, k3, *_ = oracle.realign(km, lens, ends, slot=np.array([1, 4, 5, 3], np.int32))
     assert rc == oracle.ERR_ARG and np.array_equal(k3, km)
+    rc, k4, *_ = oracle.realign(km, lens, ends, slot=np.array([1, 4, 1, 3], np.int32))   # row 1 twice
+    assert rc == oracle.ERR_ARG and np.array_equal(k4, km)
     rc, *_ = oracle.realign(km, np.array([-1, 7, 0, 5], np.int32), ends, slot=slot)
     assert rc == oracle.ERR_LENGTH

@@ -71,9 +71,13 @@ __device__ __forceinline__ int accepted_rows(const CommitDev& d, int b) {
   return valid ? d.acc[b] + 1 : 0;
 }
 
+// Slot bitmap of the duplicate check: bit (slot mod kSlotBits).
+constexpr int kSlotBits = 32768;
+
 // Block-wide computation of the plan.  All threads return the same plan.
 __device__ CommitPlan compute_commit_plan(const CommitDev& d) {
   __shared__ int s_len_bad, s_arg_bad, s_new_lmax;
+  __shared__ uint32_t s_seen[kSlotBits / 32];
   const int T = d.M + 1;
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -81,6 +85,8 @@ __device__ CommitPlan compute_commit_plan(const CommitDev& d) {
     s_arg_bad = 0;
     s_new_lmax = 0;
   }
+  if (d.slot)
+    for (int w = tid; w < kSlotBits / 32; w += blockDim.x) s_seen[w] = 0u;
   __syncthreads();
   const int old_lmax = d.mode == kRealign ? 0 : *d.lmax;
   const bool lmax_bad = d.mode != kRealign && (old_lmax < 0 || (int64_t)old_lmax > d.cap);
@@ -88,7 +94,18 @@ __device__ CommitPlan compute_commit_plan(const CommitDev& d) {
   for (int b = tid; b < d.B; b += blockDim.x) {
     const int L = d.len[b];
     const int row = d.slot ? d.slot[b] : b;
-    if (row < 0 || row >= d.rows) arg_bad = 1;
+    if (row < 0 || row >= d.rows) {
+      arg_bad = 1;
+    } else if (d.slot) {
+      // Two sequences on one pool row would shift and gather the same slabs
+      // at once.  A repeated residue is confirmed by a scan (a larger pool
+      // can map different slots to one bit).
+      const int bit = row & (kSlotBits - 1);
+      const uint32_t m = 1u << (bit & 31);
+      if (atomicOr(&s_seen[bit >> 5], m) & m)
+        for (int c = 0; c < d.B; ++c)
+          if (c != b && d.slot[c] == row) arg_bad = 1;
+    }
     if (d.mode == kRealign) {
       const int e = d.end[b];
       if (L < 0 || e < L || (int64_t)e > d.cap) len_bad = 1;
