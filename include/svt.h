@@ -133,9 +133,17 @@ int svt_expand_mask(const uint64_t* mask, const int32_t* status, const int32_t* 
 /* never read.  With seq_slot set, sequence b's cache rows are                 */
 /* k_cache[seq_slot[b]] and v_cache[seq_slot[b]] of a pool of n_slots rows     */
 /* (q, tree KV, mask and out stay indexed by b); a slot outside [0, n_slots)  */
-/* gives that sequence SVT_ERR_ARG in seq_status and zero output.  Accumulation and softmax are fp32; bf16 inputs use bf16 MFMA  */
-/* for both contractions (probabilities are rounded to bf16 for the second).  */
-/* The result is bitwise deterministic run to run.                            */
+/* gives that sequence SVT_ERR_ARG in seq_status and zero output.           */
+/* Accumulation and softmax are fp32; bf16 inputs use bf16 MFMA for both     */
+/* contractions (probabilities are rounded to bf16 for the second).  The     */
+/* result is bitwise deterministic run to run.                               */
+/* Non-finite inputs: cache columns outside the content are never read and   */
+/* may hold anything.  A key that a node does not attend never reaches that  */
+/* node's output, whatever its K values.  V of the tree rows must be finite: */
+/* masked keys enter the P V product with probability exactly 0, and 0 times */
+/* Inf or NaN is NaN (as in a dense masked attention), so a non-finite V in  */
+/* tree row j can make other rows of the same sequence and KV head non-     */
+/* finite; other sequences and KV heads are never affected.                  */
 /* ------------------------------------------------------------------------ */
 typedef struct svt_attn_args {
   int32_t B, M, Hq, Hkv, D;  /* D in {64, 128}; Hq % Hkv == 0                        */
@@ -264,8 +272,8 @@ int svt_accept_noalloc(const svt_accept_args* a, hipStream_t stream);
 /* writes the same len_out, lmax_out and commit_status.                       */
 /* With seq_slot set, sequence b lives in row seq_slot[b] of kv_main,         */
 /* tokens_main and pos_ids (pools of n_slots rows; kv_branch, tree_tokens,    */
-/* len, path, accept_len stay indexed by b).  The slots must be distinct; one */
-/* outside [0, n_slots) is SVT_ERR_ARG (checked with the accept arguments).   */
+/* len, path, accept_len stay indexed by b).  A slot outside [0, n_slots) or  */
+/* named by two sequences is SVT_ERR_ARG (checked with the accept arguments). */
 /* Rows are moved as raw bytes (any bit pattern survives).  Device-side     */
 /* errors are checked over the whole batch in this order, the first one found */
 /* goes to commit_status and then nothing is written:                         */
@@ -320,7 +328,8 @@ int svt_commit_length(const svt_commit_args* a, int32_t flags, hipStream_t strea
 /* for c < E.  *lmax = E afterwards (0 for B = 0).  Errors, found on the      */
 /* device before anything is written (then nothing is): SVT_ERR_LENGTH when   */
 /* some len[b] < 0, end[b] < len[b] or end[b] > cap, else SVT_ERR_ARG for a   */
-/* slot outside [0, n_slots).  Rows move as raw bytes.                        */
+/* slot outside [0, n_slots) or named by two sequences.  Rows move as raw     */
+/* bytes.                                                                     */
 /* ------------------------------------------------------------------------ */
 typedef struct svt_realign_args {
   int32_t B, Hkv, D, n_layers;

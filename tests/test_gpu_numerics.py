@@ -268,3 +268,54 @@ def test_argmax_ties_and_nan_across_chunks(V):
     _, ost = oracle.validate(par, M)
     oal, opath, obo = oracle.accept(am0, tok, par, M, ost)
     assert np.array_equal(al, oal) and np.array_equal(path, opath) and np.array_equal(bo, obo)
+
+
+# ------------------------------------------------------------------ non-finite tree K/V
+@pytest.mark.parametrize("dtype,form", [("bf16", svt.SVT_ATTN_SPLIT), ("bf16", svt.SVT_ATTN_STREAM),
+                                        ("fp32", svt.SVT_ATTN_SPLIT)], ids=["bf16-split", "bf16-stream", "fp32"])
+def test_attention_nonfinite_tree_kv_contract(dtype, form):
+    """svt.h: a key a node does not attend never reaches its output whatever
+    its K values (bitwise unchanged); a non-finite V in tree row j makes j's
+    own rows non-finite, as in the oracle, and leaves every other sequence and
+    KV head bitwise unchanged (rows of the same sequence and KV head that do
+    not attend j are unspecified)."""
+    w = dataclasses.replace(wl.workload(1), dtype=dtype, B=3, Hq=8, Hkv=2, D=128, M=20,
+                            qkv_sigma=(1.0 if dtype == "fp32" else wl.workload(1).qkv_sigma))
+    lens = np.array([900, 130, 700], np.int32)
+    par = wl.trees(w, 9800)
+    q, kc, vc, kt, vt = wl.attention_inputs(w, lens, 920, 9801)
+    _, out0, mk, st, _ = H.run_attention(q, kc, vc, kt, vt, par, lens, form=form)
+    base = H.from_dev(out0)
+    b, g = 1, 1
+    anc = lambda i, j: (int(mk[b, i, j // 64]) >> (j % 64)) & 1
+    children = set(par[b, 1:].tolist())
+    j = max(x for x in range(1, w.T) if x not in children)       # a leaf: attended by its own rows only
+    inf = np.float32(np.inf) if dtype == "fp32" else np.uint16(0x7F80)
+    nan = np.float32(np.nan) if dtype == "fp32" else np.uint16(0x7FC0)
+    heads = range(g * w.G, (g + 1) * w.G)
+    # non-finite K in row j: every row that does not attend j is bitwise unchanged
+    for val in (inf, nan):
+        kt2 = kt.copy()
+        kt2[b, g, j] = val
+        _, o2, _, _, _ = H.run_attention(q, kc, vc, kt2, vt, par, lens, form=form)
+        got = H.from_dev(o2)
+        for i in range(w.T):
+            if not anc(i, j):
+                assert np.array_equal(got[b, i], base[b, i]), (i, val)
+        keep = [x for x in range(w.B) if x != b]
+        assert np.array_equal(got[keep], base[keep])
+    # non-finite V in row j: j's rows are non-finite (the oracle agrees);
+    # other sequences and the other KV head are bitwise unchanged
+    vt2 = vt.copy()
+    vt2[b, g, j] = inf
+    _, o3, _, _, _ = H.run_attention(q, kc, vc, kt, vt2, par, lens, form=form)
+    got = H.from_dev(o3)
+    f = lambda x: wl.as_f32(w, x)
+    _, ref = oracle.attention(f(q), f(kc), f(vc), f(kt), f(vt2), mk, lens, int(lens.max()), st)
+    gotf = H.out_f32(w, o3)
+    for h in heads:
+        assert not np.isfinite(gotf[b, j, h]).all() and not np.isfinite(ref[b, j, h]).all()
+    keep = [x for x in range(w.B) if x != b]
+    assert np.array_equal(got[keep], base[keep])
+    other = [h for h in range(w.Hq) if h not in heads]
+    assert np.array_equal(got[b][:, other], base[b][:, other])

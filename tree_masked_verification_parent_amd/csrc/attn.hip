@@ -445,12 +445,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
       float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       lmax *= sc;  // sc > 0: the max of scaled scores
       if (__any(lmax > m_ref[qt] + kRescale)) {  // wave-uniform; first tiles, then rare
+        // only the rows over their own threshold move their reference, so a
+        // row's result never depends on another row's scores
         const float m_new = fmaxf(m_ref[qt], group_max(lmax));
-        const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
-        lacc[qt] *= alpha;
+        if (m_new > m_ref[qt] + kRescale || m_ref[qt] == kNegInf) {
+          const float alpha = m_new == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+          lacc[qt] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
-        m_ref[qt] = m_new;
+          for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= alpha;
+          m_ref[qt] = m_new;
+        }
       }
       const float neg_m = m_ref[qt] == kNegInf ? 0.0f : -m_ref[qt];
 #pragma unroll
