@@ -151,30 +151,30 @@ __device__ CommitPlan compute_commit_plan(const CommitDev& d) {
 }
 
 // Shift n elements (E = one 16-byte word or one int32) from src to src + delta
-// inside one slab.  All threads of the block take part.
-template <typename E, int U>
+// inside one slab.  All threads of the block take part.  A chunk is four
+// elements per thread, staged in four named registers (an array here ends up
+// in scratch or LDS, depending on what else the kernel allocates).
+template <typename E>
 __device__ void shift_in_place(E* __restrict__ base, int64_t src_off, int64_t n, int64_t delta) {
   if (delta == 0 || n <= 0) return;
-  constexpr int CH = 256 * U;
+  constexpr int CH = 256 * 4;
   const int tid = threadIdx.x;
   const int64_t nch = (n + CH - 1) / CH;
   E* src = base + src_off;
   E* dst = src + delta;
   for (int64_t c = 0; c < nch; ++c) {
     const int64_t ci = delta > 0 ? (nch - 1 - c) : c;
-    const int64_t lo = ci * CH;
-    E r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = lo + u * 256 + tid;
-      if (i < n) r[u] = src[i];
-    }
+    const int64_t i0 = ci * CH + tid, i1 = i0 + 256, i2 = i0 + 512, i3 = i0 + 768;
+    E r0{}, r1{}, r2{}, r3{};
+    if (i0 < n) r0 = src[i0];
+    if (i1 < n) r1 = src[i1];
+    if (i2 < n) r2 = src[i2];
+    if (i3 < n) r3 = src[i3];
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = lo + u * 256 + tid;
-      if (i < n) dst[i] = r[u];
-    }
+    if (i0 < n) dst[i0] = r0;
+    if (i1 < n) dst[i1] = r1;
+    if (i2 < n) dst[i2] = r2;
+    if (i3 < n) dst[i3] = r3;
   }
   __syncthreads();
 }
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void commit_move_kernel(CommitDev d) {
     const int h = x % d.Hkv;
     const int lp = x / d.Hkv;
     uint4* main_s = d.kv + (((int64_t)lp * d.rows + row) * d.Hkv + h) * d.cap * d.row16;
-    shift_in_place<uint4, 4>(main_s, (int64_t)src * d.row16, (int64_t)L * d.row16, (int64_t)(dst - src) * d.row16);
+    shift_in_place<uint4>(main_s, (int64_t)src * d.row16, (int64_t)L * d.row16, (int64_t)(dst - src) * d.row16);
     if (A > 0) {
       const uint4* br_s = d.br + (((int64_t)lp * d.B + b) * d.Hkv + h) * (int64_t)T * d.row16;
       uint4* out = main_s + (int64_t)app * d.row16;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void commit_move_kernel(CommitDev d) {
   } else {
     if (d.tok) {
       int32_t* tm = d.tok + (int64_t)row * d.cap;
-      shift_in_place<int32_t, 4>(tm, src, L, (int64_t)dst - src);
+      shift_in_place<int32_t>(tm, src, L, (int64_t)dst - src);
       for (int k = tid; k < A; k += 256) tm[app + k] = d.ttok[(int64_t)b * T + (pb ? pb[k] : k)];
     }
     if (d.pos) {
