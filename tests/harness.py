@@ -134,11 +134,24 @@ def stream_plan(B, T, Hq, Hkv, lens, status=None):
     return nqb, qb_rows, nw, pc
 
 
-def stream_units(B, T, Hq, Hkv, lens, grid, status=None):
+def stream_grid(B, T, Hq, Hkv, cus):
+    """Ranges of the stream form: one per CU, or for a single sequence the
+    largest whole number of ranges per unit that leaves at most a tenth of
+    the CUs idle."""
+    nqb, _, _, _ = stream_plan(B, T, Hq, Hkv, None)
+    units = Hkv * nqb
+    if B == 1 and units <= cus and 10 * units * (cus // units) >= 9 * cus:
+        return units * (cus // units)
+    return cus
+
+
+def stream_units(B, T, Hq, Hkv, lens, cus, status=None):
     """Units of the stream form in stream order, each with the range starts
-    that fall strictly inside it (a unit with cuts is merged from partials)."""
+    that fall strictly inside it (a unit with cuts is merged from partials),
+    for a device of `cus` compute units."""
     G = Hq // Hkv
     R = G * T
+    grid = stream_grid(B, T, Hq, Hkv, cus)
     nqb, qb_rows, nw, pc = stream_plan(B, T, Hq, Hkv, lens, status)
     ntree = (T + KT - 1) // KT
     tiles = []

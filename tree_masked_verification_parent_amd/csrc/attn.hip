@@ -63,14 +63,16 @@ struct AttnDev {
   const int32_t* slot;  // sequence -> cache row of k/v_cache, or NULL (identity)
   void* out;
   int32_t* seq_status;
-  float* ws_o;   // split partials [B][Hkv][ns][R][D]; stream partials [2*grid][qb_rows][D]
-  float* ws_ml;  // matching (m, l) pairs
+  float* ws_o;   // split form: partials [B][Hkv][ns][R][D]
+  float* ws_ml;  // split form: matching (m, l) pairs
+  _Float16* ws_h;  // stream form: partial O / l per row, divided by the row's scale s, [2*grid][qb_rows][D]
+  float4* ws_mls;  // stream form: (m, l, s, 0) per partial row
   int* ws_pref;  // stream form: tiles before each sequence [B + 1], then non-empty sequences before it [B + 1]
   int64_t cap;
   int B, T, Hq, Hkv, G, R, W;
   int lmax_bound, kc, ns, nqb, qb_rows, nunits;
   int n_slots;      // cache rows when slot is set
-  int stream_grid;  // workgroups of the stream form
+  int stream_grid;  // stream form: ranges of the cut (one per CU, or a whole number per unit)
   int piece_cost;   // stream form: key tiles' worth of time one unit's set-up and output cost
   float scale_log2;
 };
@@ -711,11 +713,12 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     }
     __syncthreads();
   }
-  const int G = gridDim.x;
+  const int G = a.stream_grid;  // ranges of the cut; workgroups past them (if any) get none
   // Consecutive ranges go to one XCD (the hardware sends workgroup w to XCD
   // w % 8), so the query blocks of one KV head, adjacent in the stream, tend
   // to share an L2.
-  const int c = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int NG = gridDim.x;
+  const int c = (NG % 8 == 0) ? (int)(blockIdx.x % 8) * (NG / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int UPB = a.Hkv * a.nqb;  // units per sequence
   const int64_t N = (int64_t)UPB * s_pref[B];
   // Ranges are equal in cost, not in tiles: a unit costs its key tiles plus
@@ -1071,6 +1074,20 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     else run_piece(std::integral_constant<int, 0>{}, x, pend);
 
     // ---- end of the piece; lane holds O^T[d = dt*16 + 4*grp + e][query n16]
+    // A cut piece leaves its normalised output O / l in fp16, divided by the
+    // row's largest |O / l| (s, kept in fp32 with m and l): the stored values
+    // lie in [-1, 1], so their rounding error is at most 2^-12 s, an eighth of
+    // the bf16 output's relative rounding, whatever the scale of V.
+    float pscale[QMAX];
+#pragma unroll
+    for (int qt = 0; qt < QMAX; ++qt) {
+      float am = 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(o[qt][dt][e]));
+      pscale[qt] = whole ? 0.0f : group_max(am);  // all lanes: the four lanes of a row exchange
+    }
 #pragma unroll
     for (int qt = 0; qt < QMAX; ++qt) {
       if (qt >= nlive || row_node[qt] < 0) continue;
@@ -1089,13 +1106,19 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
       } else {
         const int slot = 2 * c + (pend == hi ? 1 : 0);
         const int64_t pr = (int64_t)slot * a.qb_rows + lt * 16 + n16;
-        float* po = a.ws_o + pr * D;
+        const float l = lacc[qt][0];
+        const float s_row = l > 0.0f ? pscale[qt] / l : 0.0f;      // max |O / l| of the row
+        const float f = pscale[qt] > 0.0f ? 1.0f / pscale[qt] : 0.0f;  // O -> (O / l) / s
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        _Float16* po = a.ws_h + pr * D;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[qt][dt];
-        if (grp == 0) {
-          a.ws_ml[pr * 2 + 0] = m_ref[qt];
-          a.ws_ml[pr * 2 + 1] = lacc[qt][0];
+        for (int dt = 0; dt < NDT; ++dt) {
+          f16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (_Float16)(o[qt][dt][e] * f);
+          *reinterpret_cast<f16x4*>(po + dt * 16 + 4 * grp) = v;
         }
+        if (grp == 0) a.ws_mls[pr] = make_float4(m_ref[qt], l, s_row, 0.0f);
       }
     }
     x = pend;
@@ -1103,7 +1126,7 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   }
 
   // ---- skipped sequences: zero output rows and report why (ranges share the work)
-  for (int b = c; b < B; b += G) {
+  for (int b = c; b < B; b += NG) {
     if (s_pref[b + 1] != s_pref[b]) continue;
     int code;
     stream_seq_tiles(a, b, lmax, &code);
@@ -1183,35 +1206,35 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
     if (!row_ok) continue;
     const int np = s_np;
     for (int k = 0; k < np; k += KB) {
-      float mi[KB], li[KB], oi[KB][DPT];
+      float mi[KB], li[KB], si[KB];
+      float oi[KB][DPT];  // converted on load: the merge loop below indexes it
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         // every slot loads (past the last piece: the last piece again), so the
         // batch's loads issue back to back; only the real pieces are merged
         const int64_t pr = (int64_t)s_slot[min(k + j, np - 1)] * a.qb_rows + rl;
-        mi[j] = a.ws_ml[pr * 2];
-        li[j] = a.ws_ml[pr * 2 + 1];
-        const float* src = a.ws_o + pr * D + d0;
-        if constexpr (DPT % 4 == 0) {
+        const float4 mls = a.ws_mls[pr];
+        mi[j] = mls.x;
+        li[j] = mls.y;
+        si[j] = mls.z;
+        const _Float16* src = a.ws_h + pr * D + d0;
+        typedef _Float16 f16xN __attribute__((ext_vector_type(DPT)));
+        const f16xN v = *reinterpret_cast<const f16xN*>(src);
 #pragma unroll
-          for (int e = 0; e < DPT; e += 4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
-            oi[j][e] = v[0]; oi[j][e + 1] = v[1]; oi[j][e + 2] = v[2]; oi[j][e + 3] = v[3];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < DPT; ++e) oi[j][e] = src[e];
-        }
+        for (int e = 0; e < DPT; ++e) oi[j][e] = (float)v[e];
       }
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         if (k + j >= np) break;
-        if (mi[j] == kNegInf) continue;  // no key of this piece is visible to the row
-        const float mn = fmaxf(mx, mi[j]);
-        const float s0 = exp2f(mx - mn), s1 = exp2f(mi[j] - mn);
-        l = l * s0 + li[j] * s1;
+        const float mj = mi[j], lj = li[j], sj = si[j];
+        if (mj == kNegInf) continue;  // no key of this piece is visible to the row
+        const float mn = fmaxf(mx, mj);
+        const float s0 = exp2f(mx - mn), s1 = exp2f(mj - mn);
+        const float w = lj * s1;     // weight of the piece's normalised output
+        const float ws = w * sj;     // times its scale
+        l = l * s0 + w;
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) acc[e] = acc[e] * s0 + oi[j][e] * s1;
+        for (int e = 0; e < DPT; ++e) acc[e] = acc[e] * s0 + oi[j][e] * ws;
         mx = mn;
       }
     }
@@ -1485,6 +1508,13 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     // One workgroup per CU.
     if (cus <= 0) return false;
     p->grid = cus;
+    // With one sequence every unit holds the same tiles, so a grid of a whole
+    // number of ranges per unit puts each range inside one unit and no range
+    // pays a unit boundary (storing one piece, loading the next piece's Q);
+    // it leaves fewer than `units` CUs idle, used only when that is at most
+    // a tenth of them.
+    const int units = a->Hkv * ((p->R + p->qb_rows - 1) / p->qb_rows);
+    if (a->B == 1 && units <= cus && 10 * units * (cus / units) >= 9 * cus) p->grid = units * (cus / units);
   } else {
     p->wide = 0;
     p->nwk = 1;
@@ -1501,7 +1531,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->ns = 1;
     const size_t rows = (size_t)2 * p->grid * p->qb_rows;
     const size_t pref_bytes = ((size_t)2 * (a->B + 1) * sizeof(int) + 255) / 256 * 256;
-    p->ws_bytes = pref_bytes + rows * (a->D + 2) * sizeof(float);
+    p->ws_bytes = pref_bytes + rows * (a->D * sizeof(_Float16) + sizeof(float4));
     return true;
   }
   // Prefix split size: enough workgroups to cover the chip several times over.
@@ -1535,13 +1565,18 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   if (p.wide) {
     unsigned char* w = static_cast<unsigned char*>(a->workspace);
     const size_t pref_bytes = ((size_t)2 * (a->B + 1) * sizeof(int) + 255) / 256 * 256;
+    const size_t rows = (size_t)2 * p.grid * p.qb_rows;
     d.ws_pref = reinterpret_cast<int*>(w);
-    d.ws_o = reinterpret_cast<float*>(w + pref_bytes);
-    d.ws_ml = d.ws_o + (size_t)2 * p.grid * p.qb_rows * a->D;
+    d.ws_mls = reinterpret_cast<float4*>(w + pref_bytes);
+    d.ws_h = reinterpret_cast<_Float16*>(w + pref_bytes + rows * sizeof(float4));
+    d.ws_o = nullptr;
+    d.ws_ml = nullptr;
   } else {
     float* ws = static_cast<float*>(a->workspace);
     const size_t n_o = p.ns > 1 ? (size_t)a->B * a->Hkv * p.ns * p.R * a->D : 0;
     d.ws_pref = nullptr;
+    d.ws_h = nullptr;
+    d.ws_mls = nullptr;
     d.ws_o = ws;
     d.ws_ml = ws ? ws + n_o : nullptr;
   }
@@ -1563,7 +1598,10 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   d.scale_log2 = scale * kLog2e;
   if (p.wide) {
-    const dim3 g(p.grid);
+    // one workgroup per CU; with fewer ranges than CUs the rest get none,
+    // and the XCD-aware range order keeps its multiple of 8
+    const int cus = device_cu_count();
+    const dim3 g(cus > p.grid ? cus : p.grid);
 #define SVT_STREAM(DD)                                                                                 \
   switch (p.nw) { /* compute waves; two producer waves on top */                                       \
     case 1: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 1, 1>), g, dim3(3 * 64), 0, s, d); break;    \
