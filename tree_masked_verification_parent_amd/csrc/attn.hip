@@ -265,6 +265,60 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
   const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
   const int r0 = c.qb * a.qb_rows;
 
+  const int n_tiles = c.n_ptiles + c.n_ttiles;
+  const int pad = c.lmax - c.L;
+
+  auto tile_rows = [&](int t, const uint16_t*& kb, const uint16_t*& vb, int& nvalid) {
+    if (t < c.n_ptiles) {
+      const int k0 = c.k_beg + t * KT;
+      const int64_t col = (int64_t)pad + k0;
+      kb = kc + (c.cg * a.cap + col) * D;
+      vb = vc + (c.cg * a.cap + col) * D;
+      nvalid = min(KT, c.k_end - k0);
+    } else {
+      const int j0 = (t - c.n_ptiles) * KT;
+      kb = ktr + (bg * a.T + j0) * D;
+      vb = vtr + (bg * a.T + j0) * D;
+      nvalid = min(KT, a.T - j0);
+    }
+  };
+  // Copy tile t into stage `st`: 1 KB blocks dealt round-robin to the waves
+  // (a wave past the last block of the final round skips it and waits on
+  // its own smaller count).  Rows past the valid ones repeat the last valid
+  // row; they are masked out.
+  // Per-lane source rows and swizzled chunk offsets of this wave's copies.
+  int crow[TL::PER_WAVE], ck[TL::PER_WAVE], cv[TL::PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < TL::PER_WAVE; ++j) {
+    const int row = ((wave + NW * j) % TL::NINSTR) * TL::RPI + lane / TL::CPR;
+    const int slot = lane % TL::CPR;
+    crow[j] = row;
+    ck[j] = 8 * (slot ^ TL::swz_k(row));
+    cv[j] = 8 * (slot ^ TL::swz_v(row));
+  }
+  auto issue_tile = [&](int t, int st) {
+    const uint16_t *kb, *vb;
+    int nvalid;
+    tile_rows(t, kb, vb, nvalid);
+    unsigned char* kl = lds + st * TL::STAGEB;
+    unsigned char* vl = kl + TL::TILEB;
+#pragma unroll
+    for (int j = 0; j < TL::PER_WAVE; ++j) {
+      if (!TL::has_copy(wave, j)) continue;
+      const int ins = (wave + NW * j) % TL::NINSTR;
+      const int src = (nvalid == KT ? crow[j] : min(crow[j], nvalid - 1)) * D;
+      copy16_to_lds(kb + src + ck[j], kl + ins * 1024);
+      copy16_to_lds(vb + src + cv[j], vl + ins * 1024);
+    }
+  };
+
+  // The first tiles' copies are issued before the Q fragments and mask
+  // words are loaded, so the two travel together (the wait for Q below also
+  // covers the copies: completion is counted in issue order).
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < n_tiles) issue_tile(st, st);
+
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query row n16 of
   // each of its tiles, dims ks*32 + 8*grp .. +7.
   bf16x8 qf[QW][NKS];
@@ -342,53 +396,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
     voff[dt] = vrow * TL::ROWB + 16 * ((2 * dt + (q4 >> 1)) ^ TL::swz_v(vrow)) + 8 * (q4 & 1);
-
-  const int n_tiles = c.n_ptiles + c.n_ttiles;
-  const int pad = c.lmax - c.L;
-
-  auto tile_rows = [&](int t, const uint16_t*& kb, const uint16_t*& vb, int& nvalid) {
-    if (t < c.n_ptiles) {
-      const int k0 = c.k_beg + t * KT;
-      const int64_t col = (int64_t)pad + k0;
-      kb = kc + (c.cg * a.cap + col) * D;
-      vb = vc + (c.cg * a.cap + col) * D;
-      nvalid = min(KT, c.k_end - k0);
-    } else {
-      const int j0 = (t - c.n_ptiles) * KT;
-      kb = ktr + (bg * a.T + j0) * D;
-      vb = vtr + (bg * a.T + j0) * D;
-      nvalid = min(KT, a.T - j0);
-    }
-  };
-  // Copy tile t into stage `st`: 1 KB blocks dealt round-robin to the waves
-  // (a wave past the last block of the final round skips it and waits on
-  // its own smaller count).  Rows past the valid ones repeat the last valid
-  // row; they are masked out.
-  // Per-lane source rows and swizzled chunk offsets of this wave's copies.
-  int crow[TL::PER_WAVE], ck[TL::PER_WAVE], cv[TL::PER_WAVE];
-#pragma unroll
-  for (int j = 0; j < TL::PER_WAVE; ++j) {
-    const int row = ((wave + NW * j) % TL::NINSTR) * TL::RPI + lane / TL::CPR;
-    const int slot = lane % TL::CPR;
-    crow[j] = row;
-    ck[j] = 8 * (slot ^ TL::swz_k(row));
-    cv[j] = 8 * (slot ^ TL::swz_v(row));
-  }
-  auto issue_tile = [&](int t, int st) {
-    const uint16_t *kb, *vb;
-    int nvalid;
-    tile_rows(t, kb, vb, nvalid);
-    unsigned char* kl = lds + st * TL::STAGEB;
-    unsigned char* vl = kl + TL::TILEB;
-#pragma unroll
-    for (int j = 0; j < TL::PER_WAVE; ++j) {
-      if (!TL::has_copy(wave, j)) continue;
-      const int ins = (wave + NW * j) % TL::NINSTR;
-      const int src = (nvalid == KT ? crow[j] : min(crow[j], nvalid - 1)) * D;
-      copy16_to_lds(kb + src + ck[j], kl + ins * 1024);
-      copy16_to_lds(vb + src + cv[j], vl + ins * 1024);
-    }
-  };
 
   // One 32-key half of the current tile.  MASKED selects the path with
   // per-key validity bits (ragged tail, tree tiles); full prefix halves skip it.
@@ -473,9 +480,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
       lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qt], lacc[qt], 0, 0, 0);
   };
 
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (st < n_tiles) issue_tile(st, st);
+
 
   for (int t = 0; t < n_tiles; ++t) {
     // tile t has landed once at most the copies of later tiles are pending
@@ -1273,6 +1278,7 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
   __shared__ float ks[KT * KS];
   __shared__ float vs[KT * D];
   __shared__ float ps[4][KT];
+  __shared__ uint64_t mws[4 * RPW][4];
 
   WgCtx c;
   if (!decode_wg(a, c)) return;
@@ -1290,27 +1296,11 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
   const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
   const int r0 = c.qb * 4 * RPW;
 
-  for (int x = tid; x < 4 * RPW * D; x += 256) {
-    const int rr = x / D, d = x % D, r = r0 + rr;
-    float v = 0.0f;
-    if (r < a.R) v = q[(((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D + d];
-    qs[x] = v;
-  }
-  float m_run[RPW], l_run[RPW], o[RPW][DPL];
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    m_run[j] = kNegInf;
-    l_run[j] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[j][e] = 0.0f;
-  }
   const int n_tiles = c.n_ptiles + c.n_ttiles;
   const int pad = c.lmax - c.L;
-  for (int t = 0; t < n_tiles; ++t) {
-    const float *kb, *vb;
-    int nvalid;
-    const bool tree_tile = t >= c.n_ptiles;
-    if (!tree_tile) {
+  // Source rows of tile t: prefix columns, or (after the prefix) tree rows.
+  auto tile_src = [&](int t, const float*& kb, const float*& vb, int& nvalid) {
+    if (t < c.n_ptiles) {
       const int k0 = c.k_beg + t * KT;
       kb = kc + (c.cg * a.cap + pad + k0) * D;
       vb = vc + (c.cg * a.cap + pad + k0) * D;
@@ -1321,14 +1311,75 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
       vb = vtr + (bg * a.T + j0) * D;
       nvalid = min(KT, a.T - j0);
     }
-    __syncthreads();
-    for (int x = tid; x < KT * D; x += 256) {
-      const int row = x / D, d = x % D;
-      const bool ok = row < nvalid;
-      ks[row * KS + d] = ok ? kb[(int64_t)row * D + d] : 0.0f;
-      vs[x] = ok ? vb[(int64_t)row * D + d] : 0.0f;
+  };
+  // Tile t's K and V go to registers first (one 16-byte load per float4,
+  // all in flight together); the next tile's loads are issued before the
+  // current tile is computed on, so they overlap it.
+  constexpr int PER = KT * D / 4 / 256;  // float4 of K (and of V) per thread
+  float4 kr[PER], vr[PER];
+  auto load_tile = [&](int t) {
+    const float *kb, *vb;
+    int nvalid;
+    tile_src(t, kb, vb, nvalid);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int x = 4 * (tid + 256 * j), row = x / D, d = x % D;
+      const bool ok = row < nvalid;  // rows past the valid ones are never read (they may not exist)
+      kr[j] = ok ? *reinterpret_cast<const float4*>(kb + (int64_t)row * D + d) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      vr[j] = ok ? *reinterpret_cast<const float4*>(vb + (int64_t)row * D + d) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  if (n_tiles > 0) load_tile(0);
+  // Global loads are issued together (16-byte loads, all in flight before
+  // the first LDS write): one memory round trip per stage, not one per
+  // element.  Rows are D floats, so every 4-float group lies in one row.
+  {
+    // ancestor-mask words of the block's rows, for the tree tiles (written
+    // to LDS below, visible after the first tile's barrier)
+    uint64_t mv = 0ull;
+    if (c.n_ttiles > 0 && tid < 4 * RPW * 4) {
+      const int rr = tid / 4, w = tid % 4, r = r0 + rr;
+      if (r < a.R && w < a.W) mv = a.mask[((int64_t)c.b * a.T + r % a.T) * a.W + w];
+    }
+    constexpr int NQ4 = 4 * RPW * D / 4 / 256;  // float4 of Q per thread
+    float4 qr[NQ4];
+#pragma unroll
+    for (int j = 0; j < NQ4; ++j) {
+      const int x = 4 * (tid + 256 * j), rr = x / D, d = x % D, r = r0 + rr;
+      qr[j] = r < a.R ? *reinterpret_cast<const float4*>(
+                            q + (((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D + d)
+                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < NQ4; ++j) *reinterpret_cast<float4*>(qs + 4 * (tid + 256 * j)) = qr[j];
+    if (c.n_ttiles > 0 && tid < 4 * RPW * 4) mws[tid / 4][tid % 4] = mv;
+  }
+  float m_run[RPW], l_run[RPW], o[RPW][DPL];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    m_run[j] = kNegInf;
+    l_run[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[j][e] = 0.0f;
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const float *kb_, *vb_;
+    int nvalid;
+    tile_src(t, kb_, vb_, nvalid);
+    const bool tree_tile = t >= c.n_ptiles;
+    __syncthreads();  // the previous tile's readers are done
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int x = 4 * (tid + 256 * j), row = x / D, d = x % D;
+      float* kd = ks + row * KS + d;
+      kd[0] = kr[j].x;
+      kd[1] = kr[j].y;
+      kd[2] = kr[j].z;
+      kd[3] = kr[j].w;
+      *reinterpret_cast<float4*>(vs + x) = vr[j];
     }
     __syncthreads();
+    if (t + 1 < n_tiles) load_tile(t + 1);
 #pragma unroll 1
     for (int j = 0; j < RPW; ++j) {
       const int rr = wave * RPW + j, r = r0 + rr;
@@ -1336,7 +1387,7 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
       const int node = r % a.T;
       bool ok = lane < nvalid;
       if (tree_tile) {
-        const uint64_t mw = a.mask[((int64_t)c.b * a.T + node) * a.W + (t - c.n_ptiles)];
+        const uint64_t mw = mws[rr][t - c.n_ptiles];
         ok = ok && ((mw >> lane) & 1ull);
       }
       float s = 0.0f;
