@@ -121,24 +121,30 @@ class StreamUnit:
     cuts: list         # stream tiles inside (base, base + ntl) where a range starts
 
 
-def stream_plan(B, T, Hq, Hkv, lens, status=None):
-    """(nqb, qb_rows, compute waves, set-up charge) of the stream form."""
+def stream_plan(B, T, Hq, Hkv, cus):
+    """(nqb, qb_rows, compute waves, set-up charge) of the stream form: at
+    most 12 query tiles per unit, 8 when the batch has fewer units than CUs;
+    the units of a KV head split its tiles as evenly as whole tiles allow."""
     R = (Hq // Hkv) * T
     nqt = (R + 15) // 16
-    nqb0 = (nqt + 11) // 12
-    tpb = (nqt + nqb0 - 1) // nqb0
-    nw = tpb if tpb <= 2 else 4 if tpb <= 4 else 6 if tpb <= 6 else 9 if tpb <= 9 else 12
+    cap = 8 if B * Hkv * ((nqt + 11) // 12) < cus else 12
+    nqb = (nqt + cap - 1) // cap
+    tpb = (nqt + nqb - 1) // nqb
+    nw = tpb if tpb <= 2 else 4 if tpb <= 4 else 6 if tpb <= 6 else 8 if tpb <= 8 else 9 if tpb <= 9 else 12
     pc = 5 if nw >= 9 else 2
-    qb_rows = tpb * 16
-    nqb = (R + qb_rows - 1) // qb_rows
-    return nqb, qb_rows, nw, pc
+    return nqb, tpb * 16, nw, pc
+
+
+def unit_rows(nqt, nqb, qb, R):
+    """Query rows [lo, hi) of query block qb of a KV head."""
+    return 16 * ((qb * nqt) // nqb), min(R, 16 * (((qb + 1) * nqt) // nqb))
 
 
 def stream_grid(B, T, Hq, Hkv, cus):
     """Ranges of the stream form: one per CU, or for a single sequence the
     largest whole number of ranges per unit that leaves at most a tenth of
     the CUs idle."""
-    nqb, _, _, _ = stream_plan(B, T, Hq, Hkv, None)
+    nqb, _, _, _ = stream_plan(B, T, Hq, Hkv, cus)
     units = Hkv * nqb
     if B == 1 and units <= cus and 10 * units * (cus // units) >= 9 * cus:
         return units * (cus // units)
@@ -152,7 +158,8 @@ def stream_units(B, T, Hq, Hkv, lens, cus, status=None):
     G = Hq // Hkv
     R = G * T
     grid = stream_grid(B, T, Hq, Hkv, cus)
-    nqb, qb_rows, nw, pc = stream_plan(B, T, Hq, Hkv, lens, status)
+    nqb, qb_rows, nw, pc = stream_plan(B, T, Hq, Hkv, cus)
+    nqt = (R + 15) // 16
     ntree = (T + KT - 1) // KT
     tiles = []
     for b in range(B):
@@ -196,7 +203,7 @@ def stream_units(B, T, Hq, Hkv, lens, cus, status=None):
             base = upb * pref[b] + j * ntl
             g, qb = divmod(j, nqb)
             cuts = [x for x in starts if base < x < base + ntl]
-            units.append(StreamUnit(b, g, qb, base, ntl, ntl - ntree, qb * qb_rows, min(R, (qb + 1) * qb_rows), cuts))
+            units.append(StreamUnit(b, g, qb, base, ntl, ntl - ntree, *unit_rows(nqt, nqb, qb, R), cuts))
     return units
 
 

@@ -336,6 +336,18 @@ ATTN_CASES = [
     ("bf16-d64-mha-2tiles", dict(B=3, dtype="bf16", Hq=2, Hkv=2, D=64, M=20), [650, 3, 1200]),
     ("bf16-d64-gqa2-4tiles", dict(B=2, dtype="bf16", Hq=4, Hkv=2, D=64, M=31), [900, 2500]),
     ("bf16-d64-gqa16-12tiles", dict(B=2, dtype="bf16", Hq=16, Hkv=1, D=64, M=11), [1700, 400]),
+    # fewer units than CUs: at most 8 query tiles per unit, the eight-wave
+    # stream form; 13 tiles per KV head split 6 + 7 over two units
+    ("bf16-d128-gqa4-8tiles", dict(B=1, dtype="bf16", Hq=8, Hkv=2, D=128, M=31), [2300]),
+    ("bf16-d64-gqa4-13tiles", dict(B=2, dtype="bf16", Hq=8, Hkv=2, D=64, M=51), [1900, 333]),
+    # at least as many units as CUs: up to 12 query tiles per unit, the nine-
+    # and twelve-wave stream forms at both head dims
+    ("bf16-d64-b32-9tiles", dict(B=32, dtype="bf16", Hq=32, Hkv=8, D=64, M=32),
+     [64 + (37 * i) % 600 for i in range(32)]),
+    ("bf16-d128-b32-12tiles", dict(B=32, dtype="bf16", Hq=32, Hkv=8, D=128, M=47),
+     [1 + (53 * i) % 700 for i in range(32)]),
+    ("bf16-d64-b32-12tiles", dict(B=32, dtype="bf16", Hq=32, Hkv=8, D=64, M=44),
+     [(71 * i) % 650 for i in range(31)] + [650]),
 ]
 
 

@@ -73,9 +73,16 @@ struct AttnDev {
   int lmax_bound, kc, ns, nqb, qb_rows, nunits;
   int n_slots;      // cache rows when slot is set
   int stream_grid;  // stream form: ranges of the cut (one per CU, or a whole number per unit)
+  int rpu;          // stream form: ranges per unit when the grid is a whole number of them per unit, else 0
+  int nqt;          // 16-row query tiles per KV head
   int piece_cost;   // stream form: key tiles' worth of time one unit's set-up and output cost
   float scale_log2;
 };
+
+// Stream form: query block qb of a KV head holds query tiles
+// [unit_tile_lo(qb), unit_tile_lo(qb + 1)); the nqb blocks split the nqt tiles
+// as evenly as whole tiles allow.
+__device__ __forceinline__ int unit_tile_lo(const AttnDev& a, int qb) { return (int)(((int64_t)qb * a.nqt) / a.nqb); }
 
 // Why sequence b is skipped (SVT_OK: it is not): its tree status, a cache
 // row outside the pool, or lengths outside 0 <= len <= lmax <= lmax_bound.
@@ -645,6 +652,54 @@ __device__ __forceinline__ int64_t stream_lo(int64_t c, int64_t n, int g) { retu
 // Range holding stream tile x.
 __device__ __forceinline__ int stream_range_of(int64_t x, int64_t n, int g) { return (int)div_floor((x + 1) * g - 1, n); }
 
+// The ranges that hold tiles of one unit.  The unit's cost interval is
+// [cu, cu + pc + ntl) (its set-up, then its tiles) and its tiles are stream
+// tiles [p, p + ntl); the ranges are g equal cuts of the total cost ct, and a
+// range boundary at cost q inside the unit's tiles falls before tile
+// p + (q - cu - pc).  Ranges c0..c1 touch the unit.
+struct UnitCut {
+  int64_t ct, cu, p;
+  int g, pc, ntl, c0, c1;
+};
+__device__ __forceinline__ UnitCut unit_cut(int64_t ct, int64_t cu, int64_t p, int g, int pc, int ntl) {
+  UnitCut u{ct, cu, p, g, pc, ntl, 0, 0};
+  u.c0 = stream_range_of(cu + pc, ct, g);
+  u.c1 = stream_range_of(cu + pc + ntl - 1, ct, g);
+  return u;
+}
+// Whether range cc (c0 <= cc <= c1) holds a piece of the unit (ranges between
+// c0 and c1 may be empty when there are fewer tiles than ranges), and the
+// partial slot that piece leaves: 2cc + 1 when it ends at the range's end,
+// 2cc when it ends at the unit's end inside the range.  The last range ends
+// at the unit's end exactly when its cost end reaches no further than the
+// next unit's first tile.
+__device__ __forceinline__ bool unit_piece(const UnitCut& u, int cc, int* slot) {
+  const int64_t clo = stream_lo(cc, u.ct, u.g), chi = stream_lo(cc + 1, u.ct, u.g);
+  const int64_t tlo = cc == u.c0 ? u.p : u.p + (clo - u.cu - u.pc);
+  const int64_t thi = cc < u.c1 ? u.p + (chi - u.cu - u.pc) : u.p + u.ntl;
+  *slot = 2 * cc + ((cc < u.c1 || chi <= u.cu + u.ntl + 2 * (int64_t)u.pc) ? 1 : 0);
+  return tlo < thi;
+}
+
+// One step of the in-order merge of a row's pieces: (mx, l, acc) holds the
+// merged maximum (base 2), weight and output of the pieces so far; the piece
+// brings its maximum mj, its weight lj, its output divided by lj and by its
+// scale sj (oi) and that scale.  A piece that sees no key of the row has
+// mj = -inf and is skipped.
+template <int N>
+__device__ __forceinline__ void merge_piece(float& mx, float& l, float (&acc)[N], float mj, float lj, float sj,
+                                            const float (&oi)[N]) {
+  if (mj == kNegInf) return;
+  const float mn = fmaxf(mx, mj);
+  const float s0 = exp2f(mx - mn), s1 = exp2f(mj - mn);
+  const float w = lj * s1;  // weight of the piece's normalised output
+  const float ws = w * sj;  // times its scale
+  l = l * s0 + w;
+#pragma unroll
+  for (int e = 0; e < N; ++e) acc[e] = acc[e] * s0 + oi[e] * ws;
+  mx = mn;
+}
+
 // NW compute waves (QMAX query tiles each) and two producer waves.
 template <int D, int NW, int QMAX>
 __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev a) {
@@ -671,6 +726,16 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   const int grp = lane >> 4;
   const int B = a.B;
   const int lmax = *a.lmax;
+  // With nine or twelve compute waves, waves 4..7 run each tile half a step
+  // behind the others (see run_piece): waves w, w + 4, w + 8 share a SIMD, so
+  // every SIMD then holds a lagging and a leading wave whose matrix and
+  // vector phases overlap instead of coinciding after every barrier (B=1 32K
+  // with twelve: 59.6 -> 56.9 us per call; with eight waves it was slower).
+#ifndef SVT_STREAM_LAG
+#define SVT_STREAM_LAG 1
+#endif
+  constexpr bool kLagging = SVT_STREAM_LAG && (NW == 9 || NW == 12);
+  const bool lag = kLagging && wave < NW && ((wave >> 2) & 1);
 
   // ---- per-sequence tile counts and their prefix (every workgroup computes it)
   if (tid == 0) {
@@ -723,7 +788,15 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   // w % 8), so the query blocks of one KV head, adjacent in the stream, tend
   // to share an L2.
   const int NG = gridDim.x;
-  const int c = (NG % 8 == 0) ? (int)(blockIdx.x % 8) * (NG / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  int c = (NG % 8 == 0) ? (int)(blockIdx.x % 8) * (NG / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  if (a.rpu > 0 && c < G) {
+    // A whole number of ranges per unit (one sequence): consecutive
+    // workgroup slots take the same key range of every query block of a KV
+    // head, so the workgroups of one XCD read the same K/V tiles at about the
+    // same time and its L2 serves all but the first read of each.
+    const int qb = c % a.nqb, r = (c / a.nqb) % a.rpu, g = c / (a.nqb * a.rpu);
+    c = (g * a.nqb + qb) * a.rpu + r;
+  }
   const int UPB = a.Hkv * a.nqb;  // units per sequence
   const int64_t N = (int64_t)UPB * s_pref[B];
   // Ranges are equal in cost, not in tiles: a unit costs its key tiles plus
@@ -758,7 +831,6 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.vcache);
   const uint16_t* __restrict__ ktr = static_cast<const uint16_t*>(a.ktree);
   const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
-  const int tpb = a.qb_rows / 16;
 
   // Cursor over the stream: unit (b, j = g*nqb + qb), its first tile `base`,
   // its tile count, and what the per-tile source addresses need (content
@@ -1004,28 +1076,48 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
       for (int64_t x = x0; x < x1; ++x) landed(x);
     } else {
       f32x4 sa[NQ][4];
-      for (int64_t x = x0; x < x1; ++x) {
-        landed(x);
-        scores(nq_c, x, sa);
-        finish(nq_c, x, sa);
+      if (!lag) {
+        for (int64_t x = x0; x < x1; ++x) {
+          landed(x);
+          scores(nq_c, x, sa);
+          finish(nq_c, x, sa);
+        }
+      } else {
+        // Lagging wave: between barriers x and x + 1 it finishes tile x - 1
+        // (softmax, P V) and then computes the scores of tile x, so its
+        // matrix work falls where the leading waves run their softmax.
+        for (int64_t x = x0; x < x1; ++x) {
+          landed(x);
+          if (x > x0) finish(nq_c, x - 1, sa);
+          scores(nq_c, x, sa);
+        }
+        finish(nq_c, x1 - 1, sa);
       }
     }
   };
 
   if (wave >= NW) {
-    // Producer: three tiles ahead.  Before barrier y it waits for its copies
-    // of tile y (tiles y + 1 and y + 2 may still be in flight); after it, it
-    // issues tile y + 3 into the stage of tile y - 1, which every compute
-    // wave finished before arriving at barrier y.
+    // Producer of K: three tiles ahead.  Before barrier y it waits for its
+    // copies of tile y (tiles y + 1 and y + 2 may still be in flight); after
+    // it, it issues tile y + 3 into the stage of tile y - 1, whose K every
+    // compute wave read before arriving at barrier y.  Producer of V: two
+    // tiles ahead when some compute waves lag (they read V of tile y - 1
+    // between barriers y and y + 1), so tile y + 2 goes into the stage of
+    // tile y - 2; three ahead otherwise.
+    const bool two_ahead = pw == 1 && kLagging;
     if (lo < hi) produce(0);
     if (lo + 1 < hi) produce(1);
-    if (lo + 2 < hi) produce(2);
+    if (!two_ahead && lo + 2 < hi) produce(2);
     for (int64_t y = lo; y < hi; ++y) {
-      if (y + 2 < hi) wait_vmcnt<2 * TL::NINSTR>();
+      if (!two_ahead && y + 2 < hi) wait_vmcnt<2 * TL::NINSTR>();
       else if (y + 1 < hi) wait_vmcnt<TL::NINSTR>();
       else wait_vmcnt<0>();
       lds_barrier();
-      if (y + 3 < hi) produce((int)((y - lo + 3) % kStages));
+      if (two_ahead) {
+        if (y + 2 < hi) produce((int)((y - lo + 2) % kStages));
+      } else if (y + 3 < hi) {
+        produce((int)((y - lo + 3) % kStages));
+      }
     }
   } else
   for (int64_t x = lo; x < hi;) {
@@ -1033,12 +1125,14 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     const int64_t pend = min(hi, cur.base + (int64_t)cur.ntl);
     const bool whole = x == cur.base && pend == cur.base + cur.ntl;
     const int g = cur.j / a.nqb, qb = cur.j % a.nqb;
-    const int r0 = qb * a.qb_rows;
+    const int t0 = unit_tile_lo(a, qb);
+    const int ntq = unit_tile_lo(a, qb + 1) - t0;  // query tiles of this unit
+    const int r0 = 16 * t0;
     int nlive = 0;
 #pragma unroll
     for (int qt = 0; qt < QMAX; ++qt) {
       const int lt = wave + NW * qt;
-      const bool live = lt < tpb && r0 + lt * 16 < a.R;
+      const bool live = lt < ntq;
       nlive += live ? 1 : 0;
       const int r = r0 + lt * 16 + n16;
       const bool ok = live && r < a.R;
@@ -1095,9 +1189,11 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     }
 #pragma unroll
     for (int qt = 0; qt < QMAX; ++qt) {
-      if (qt >= nlive || row_node[qt] < 0) continue;
+      if (qt >= nlive) continue;
+      const bool rowok = row_node[qt] >= 0;  // rows past R: no output, no partial
       const int lt = wave + NW * qt;
       if (whole) {
+        if (!rowok) continue;
         const float inv = 1.0f / lacc[qt][0];
         __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)cur.b * a.T + row_node[qt]) * a.Hq + row_head[qt]) * D;
 #pragma unroll
@@ -1116,14 +1212,17 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
         const float f = pscale[qt] > 0.0f ? 1.0f / pscale[qt] : 0.0f;  // O -> (O / l) / s
         typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
         _Float16* po = a.ws_h + pr * D;
+        f16x4 v16[NDT];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          f16x4 v;
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (_Float16)(o[qt][dt][e] * f);
-          *reinterpret_cast<f16x4*>(po + dt * 16 + 4 * grp) = v;
+          for (int e = 0; e < 4; ++e) v16[dt][e] = (_Float16)(o[qt][dt][e] * f);
+        const float4 mls = make_float4(m_ref[qt], l, s_row, 0.0f);
+        if (rowok) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f16x4*>(po + dt * 16 + 4 * grp) = v16[dt];
+          if (grp == 0) a.ws_mls[pr] = mls;
         }
-        if (grp == 0) a.ws_mls[pr] = make_float4(m_ref[qt], l, s_row, 0.0f);
       }
     }
     x = pend;
@@ -1171,15 +1270,16 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   const int64_t CT = (int64_t)UPB * ((int64_t)pref[a.B] + (int64_t)PC * npref[a.B]);
   const int64_t CU = (int64_t)UPB * ((int64_t)pref[b] + (int64_t)PC * npref[b]) + (int64_t)(g * a.nqb + qb) * (ntl + PC);
   const int64_t P = (int64_t)UPB * pref[b] + (int64_t)(g * a.nqb + qb) * ntl;
-  const int64_t E = P + ntl;
-  const int c0 = stream_range_of(CU + PC, CT, G), c1 = stream_range_of(CU + PC + ntl - 1, CT, G);
+  const UnitCut uc = unit_cut(CT, CU, P, G, PC, ntl);
+  const int c0 = uc.c0, c1 = uc.c1;
   if (c0 == c1) return;
   __shared__ int s_slot[kMaxPieces];
   __shared__ int s_np;
   const int rl = blockIdx.y * RPW + threadIdx.x / TPR;
   const int d0 = (threadIdx.x % TPR) * DPT;
-  const int r = qb * a.qb_rows + rl;
-  const bool row_ok = rl < a.qb_rows && r < a.R;
+  const int t0 = unit_tile_lo(a, qb);
+  const int r = 16 * t0 + rl;
+  const bool row_ok = rl < 16 * (unit_tile_lo(a, qb + 1) - t0) && r < a.R;
   // Online merge in range order (deterministic); ranges between c0 and c1
   // may be empty (fewer tiles than workgroups) and hold no piece.
   float mx = kNegInf, l = 0.0f;
@@ -1190,18 +1290,8 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
     __syncthreads();
     if (threadIdx.x < kMaxPieces) {
       const int cc = cs + (int)threadIdx.x;
-      bool has = false;
       int slot = 0;
-      if (cc <= c1) {
-        // tiles of range cc inside the unit: [tlo, thi); the last range ends
-        // at the unit's end exactly when its cost end reaches no further
-        // than the next unit's first tile
-        const int64_t clo = stream_lo(cc, CT, G), chi = stream_lo(cc + 1, CT, G);
-        const int64_t tlo = cc == c0 ? P : P + (clo - CU - PC);
-        const int64_t thi = cc < c1 ? P + (chi - CU - PC) : E;
-        has = tlo < thi;
-        slot = 2 * cc + ((cc < c1 || chi <= CU + ntl + 2 * (int64_t)PC) ? 1 : 0);
-      }
+      const bool has = cc <= c1 && unit_piece(uc, cc, &slot);
       const uint64_t bal = __ballot(has);
       const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
       if (has) s_slot[below] = slot;
@@ -1231,16 +1321,7 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         if (k + j >= np) break;
-        const float mj = mi[j], lj = li[j], sj = si[j];
-        if (mj == kNegInf) continue;  // no key of this piece is visible to the row
-        const float mn = fmaxf(mx, mj);
-        const float s0 = exp2f(mx - mn), s1 = exp2f(mj - mn);
-        const float w = lj * s1;     // weight of the piece's normalised output
-        const float ws = w * sj;     // times its scale
-        l = l * s0 + w;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) acc[e] = acc[e] * s0 + oi[j][e] * ws;
-        mx = mn;
+        merge_piece(mx, l, acc, mi[j], li[j], si[j], oi[j]);
       }
     }
   }
@@ -1516,6 +1597,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   p->R = p->G * p->T;
   p->nqt = (p->R + 15) / 16;
   p->grid = 0;
+  p->rpu = 0;
   p->piece_cost = 0;
   // Key tiles the stream form would hold at most (host bound).
   const int64_t stream_tiles = (int64_t)a->B * a->Hkv * ((p->nqt + 11) / 12) *
@@ -1541,12 +1623,21 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   } else if (a->dtype == SVT_BF16) {
     // Stream form: up to 12 query tiles per unit, spread evenly over the
     // fewest units per KV head, one tile per compute wave (plus the two
-    // producer waves); one workgroup per CU.
-    const int nqb = (p->nqt + 11) / 12;
+    // producer waves); one workgroup per CU.  With fewer units than CUs
+    // (one long sequence: every unit is cut into many pieces and the key
+    // tiles stream from L2) units of at most 8 tiles are faster: B=1 32K
+    // 56.6 -> 53.8 us per call against 12.
+#ifndef SVT_STREAM_FEW_TPB
+#define SVT_STREAM_FEW_TPB 8
+#endif
+    int cap_t = 12;
+    if ((int64_t)a->B * a->Hkv * ((p->nqt + 11) / 12) < (int64_t)cus) cap_t = SVT_STREAM_FEW_TPB;
+    const int nqb = (p->nqt + cap_t - 1) / cap_t;
     const int tpb = (p->nqt + nqb - 1) / nqb;
     p->wide = 1;
-    p->nw = tpb <= 2 ? tpb : tpb <= 4 ? 4 : tpb <= 6 ? 6 : tpb <= 9 ? 9 : 12;
+    p->nw = tpb <= 2 ? tpb : tpb <= 4 ? 4 : tpb <= 6 ? 6 : tpb <= 8 ? 8 : tpb <= 9 ? 9 : 12;
     p->qw = 1;
+    p->nqb = nqb;
     p->nwk = 1;
     p->stages = 4;
     p->qb_rows = tpb * 16;
@@ -1564,8 +1655,12 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     // pays a unit boundary (storing one piece, loading the next piece's Q);
     // it leaves fewer than `units` CUs idle, used only when that is at most
     // a tenth of them.
-    const int units = a->Hkv * ((p->R + p->qb_rows - 1) / p->qb_rows);
-    if (a->B == 1 && units <= cus && 10 * units * (cus / units) >= 9 * cus) p->grid = units * (cus / units);
+    const int units = a->Hkv * p->nqb;
+    p->rpu = 0;
+    if (a->B == 1 && units <= cus && 10 * units * (cus / units) >= 9 * cus) {
+      p->grid = units * (cus / units);
+      p->rpu = cus / units;
+    }
   } else {
     p->wide = 0;
     p->nwk = 1;
@@ -1574,7 +1669,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     p->stages = 1;
     p->qb_rows = 4 * kFp32RowsPerWave;
   }
-  p->nqb = (p->R + p->qb_rows - 1) / p->qb_rows;
+  if (!p->wide) p->nqb = (p->R + p->qb_rows - 1) / p->qb_rows;
   if (p->wide) {
     // Partials: two slots of qb_rows rows per workgroup, plus the prefix of
     // tiles per sequence.
@@ -1632,6 +1727,7 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     d.ws_ml = ws ? ws + n_o : nullptr;
   }
   d.stream_grid = p.grid;
+  d.rpu = p.wide ? p.rpu : 0;
   d.piece_cost = p.piece_cost;
   d.cap = a->cap;
   d.B = a->B;
@@ -1646,6 +1742,7 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.ns = p.ns;
   d.nqb = p.nqb;
   d.qb_rows = p.qb_rows;
+  d.nqt = p.nqt;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   d.scale_log2 = scale * kLog2e;
   if (p.wide) {
@@ -1653,13 +1750,14 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     // and the XCD-aware range order keeps its multiple of 8
     const int cus = device_cu_count();
     const dim3 g(cus > p.grid ? cus : p.grid);
-#define SVT_STREAM(DD)                                                                                 \
-  switch (p.nw) { /* compute waves; two producer waves on top */                                       \
-    case 1: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 1, 1>), g, dim3(3 * 64), 0, s, d); break;    \
-    case 2: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 2, 1>), g, dim3(4 * 64), 0, s, d); break;    \
-    case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4, 1>), g, dim3(6 * 64), 0, s, d); break;    \
-    case 6: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6, 1>), g, dim3(8 * 64), 0, s, d); break;    \
-    case 9: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 9, 1>), g, dim3(11 * 64), 0, s, d); break;   \
+#define SVT_STREAM(DD)                                                                             \
+  switch (p.nw) { /* compute waves; two producer waves on top */                                          \
+    case 1: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 1, 1>), g, dim3(3 * 64), 0, s, d); break;   \
+    case 2: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 2, 1>), g, dim3(4 * 64), 0, s, d); break;   \
+    case 4: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 4, 1>), g, dim3(6 * 64), 0, s, d); break;   \
+    case 6: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 6, 1>), g, dim3(8 * 64), 0, s, d); break;   \
+    case 8: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 8, 1>), g, dim3(10 * 64), 0, s, d); break;  \
+    case 9: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 9, 1>), g, dim3(11 * 64), 0, s, d); break;  \
     default: hipLaunchKernelGGL((attn_bf16_stream_kernel<DD, 12, 1>), g, dim3(14 * 64), 0, s, d); break; \
   }
     if (a->D == 128) { SVT_STREAM(128) } else { SVT_STREAM(64) }

@@ -20,6 +20,7 @@ struct AttnPlan {
   int nqt;           // 16-row query tiles per KV head
   int wide;          // bf16: 1 = stream form (one workgroup per CU over the tile stream)
   int grid;          // stream form: workgroups (compute units)
+  int rpu;           // stream form: ranges per unit when grid is a whole number of them per unit, else 0
   int qw;            // query tiles per wave (bf16 path)
   int stages;        // LDS ring depth, 2 or 4 (bf16 path)
   int nw;            // waves per workgroup (bf16 path)
