@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--pipeline", action="store_true",
                     help="round time of the B=32 workload with the commit of each round overlapped layer by layer "
                          "with the next round's attention (eager and HIP graph) against sequential rounds")
+    ap.add_argument("--eager", action="store_true",
+                    help="time steps launched call by call from the host (per-call events then include any time "
+                         "the GPU waits for the next launch) instead of replays of one HIP graph of the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 3 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -117,7 +120,8 @@ def device_copy_gbps(torch, nbytes=1 << 30, reps=5):
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache
 
 
-def cold_attention(torch, svt, r, len0, lmax0_t, attn_bytes, attn_flops, total=1 << 30, max_copies=256):
+def cold_attention(torch, svt, r, len0, lmax0_t, attn_bytes, attn_flops, total=1 << 30, max_copies=256,
+                   eager=False):
     """Attention timed over copies of one layer's inputs (Q, prefix and tree
     K/V, output) totalling at least `total` bytes of attention reads, cycled
     so that no call finds its inputs in the Infinity Cache.  The round above
@@ -138,15 +142,28 @@ def cold_attention(torch, svt, r, len0, lmax0_t, attn_bytes, attn_flops, total=1
     for a in args:  # one untimed pass
         assert svt.svt_verify_attention(a) == 0
     passes = max(1, -(-64 // n))
+    # the calls are replayed from one HIP graph (unless eager), so the GPU
+    # does not wait for the host between calls
+    g = None
+    if not eager:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for a in args:
+                assert svt.svt_verify_attention(a) == 0
+        g.replay()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(passes):
-        for a in args:
-            svt.svt_verify_attention(a)
+        if g is not None:
+            g.replay()
+        else:
+            for a in args:
+                svt.svt_verify_attention(a)
     e1.record()
     e1.synchronize()
     t = e0.elapsed_time(e1) * 1e-3 / (passes * n)
+    del g
     del keep, args
     torch.cuda.empty_cache()
     return {"copies": n, "calls": passes * n, "us_per_call": t * 1e6, "GBps": attn_bytes / t / 1e9,
@@ -781,24 +798,101 @@ def main():
     def per_step(i, j, div=1):
         return np.array([evs[k][i].elapsed_time(evs[k][j]) for k in range(args.steps)]) * 1e-3 / div
 
-    def dur(i, j, div=1):
-        return float(np.mean(per_step(i, j, div)))
-
-    def dist_us(i, j, div=1):
-        x = per_step(i, j, div) * 1e6
+    def dist_us(x):
+        x = np.asarray(x) * 1e6
         return {"mean": float(x.mean()), "p10": float(np.percentile(x, 10)), "p50": float(np.median(x)),
                 "p90": float(np.percentile(x, 90)), "min": float(x.min()), "max": float(x.max())}
 
-    t_mask = dur(0, 1)
-    t_attn = dur(1, 2, L)
-    t_accept = dur(2, 3)
-    t_commit = dur(3, 4)
-    ms_per_step = elapsed / args.steps * 1e3
-    # distribution over the timed steps of each call type (attention: the
-    # step's mean per layer) and of the whole step between its first and
-    # last event
-    timing = {"steps": args.steps, "mask_us": dist_us(0, 1), "attention_us_per_layer": dist_us(1, 2, L),
-              "accept_us": dist_us(2, 3), "commit_us": dist_us(3, 4), "step_us": dist_us(0, 4)}
+    # launched call by call: the distribution over the timed steps of each
+    # call type (attention: the step's mean per layer) and of the whole step
+    # between its first and last event
+    timing_eager = {"mode": "eager", "steps": args.steps, "mask_us": dist_us(per_step(0, 1)),
+                    "attention_us_per_layer": dist_us(per_step(1, 2, L)), "accept_us": dist_us(per_step(2, 3)),
+                    "commit_us": dist_us(per_step(3, 4)), "step_us": dist_us(per_step(0, 4)),
+                    "ms_per_step": elapsed / args.steps * 1e3}
+    if args.eager:
+        ms_per_step = elapsed / args.steps * 1e3
+        timing = timing_eager
+        t_mask, t_attn, t_accept, t_commit = (float(np.mean(per_step(i, i + 1, L if i == 1 else 1)))
+                                              for i in range(4))
+    else:
+        # The step as one HIP graph (the library allocates nothing and never
+        # synchronises, so every call captures): a serving loop launches a
+        # round this way, and the GPU never waits for the host between calls.
+        # Per-call times come from graphs of n back-to-back calls of one kind
+        # (events around each replay, on the stream the kernels run on); the
+        # commit's graph restores the lengths before each call, and a graph of
+        # the restores alone is subtracted.
+        def capture(fn, n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(n):
+                    assert fn() == 0
+            return g
+
+        def graph_s(fn, n, reps=7):
+            """Seconds per call of fn, one value per replay of a graph of n calls."""
+            g = capture(fn, n)
+            g.replay()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in ev:
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3 / n
+
+        def reps_for(t_est, calls=1):
+            # about 2 ms of work per replay
+            return int(max(1, min(200, np.ceil(2e-3 / max(t_est * calls, 1e-7)))))
+
+        g_step = capture(one_step, 1)
+        for _ in range(args.warmup):
+            g_step.replay()
+        torch.cuda.synchronize()
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            sev[k][0].record(stream)
+            g_step.replay()
+            sev[k][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        assert r.commit_status.item() == 0
+        assert np.array_equal(r.len.cpu().numpy(), lens0 + A)
+        ms_per_step = elapsed / args.steps * 1e3
+        step_s = np.array([a.elapsed_time(b) for a, b in sev]) * 1e-3
+
+        def restore():
+            r.len.copy_(len0)
+            r.lmax.copy_(lmax0_t)
+            return 0
+
+        def restore_commit():
+            restore()
+            return r.commit()
+
+        def layers():
+            rc = 0
+            for layer in range(L):
+                rc = rc or r.attention(layer)
+            return rc
+
+        restore()  # the lengths the timed calls start from (a step leaves them committed)
+        x_mask = graph_s(r.build_mask, reps_for(float(np.mean(per_step(0, 1)))))
+        x_attn = graph_s(layers, reps_for(float(np.mean(per_step(1, 2, L))), L)) / L
+        x_accept = graph_s(r.accept, reps_for(float(np.mean(per_step(2, 3)))))
+        n_c = reps_for(float(np.mean(per_step(3, 4))))
+        x_commit = graph_s(restore_commit, n_c) - float(np.median(graph_s(restore, n_c)))
+        assert r.commit_status.item() == 0
+        restore()
+        t_mask, t_attn, t_accept, t_commit = (float(np.mean(x)) for x in (x_mask, x_attn, x_accept, x_commit))
+        timing = {"mode": "graph", "steps": args.steps, "mask_us": dist_us(x_mask),
+                  "attention_us_per_layer": dist_us(x_attn), "accept_us": dist_us(x_accept),
+                  "commit_us": dist_us(x_commit), "step_us": dist_us(step_s),
+                  "ms_per_step_gpu": float(np.mean(step_s)) * 1e3,
+                  "per_call": "one value per replay of a graph of back-to-back calls of that kind, divided by the calls"}
 
     attn_bytes = algorithmic_bytes_attention(w, lens0, w.T)
     attn_flops = flops_attention(w, lens0, depth)
@@ -858,6 +952,7 @@ def main():
         "mask_us": t_mask * 1e6,
         "verified_nodes_per_s_one_layer": w.B * w.M / (t_mask + t_attn + t_accept),
         "timing": timing,
+        "timing_eager": timing_eager,
         "dominant": dominant,
         "roofline": roof(dominant),
         "roofline_attention": roof("attention"),
@@ -872,7 +967,7 @@ def main():
     out["attn_bytes_per_round_MB"] = attn_bytes * L / 1e6
     out["attn_inputs_fit_infinity_cache"] = bool(attn_bytes * L <= MALL_BYTES)
     if attn_bytes * L < (1 << 30):
-        out["attention_cold"] = cold_attention(torch, svt, r, len0, lmax0_t, attn_bytes, attn_flops)
+        out["attention_cold"] = cold_attention(torch, svt, r, len0, lmax0_t, attn_bytes, attn_flops, eager=args.eager)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, parents, lens0, logits, tokens, seed, args.cpu_seconds)
     print(json.dumps(out), flush=True)

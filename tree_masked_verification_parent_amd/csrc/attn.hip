@@ -71,6 +71,7 @@ struct AttnDev {
   int64_t cap;
   int B, T, Hq, Hkv, G, R, W;
   int lmax_bound, kc, ns, nqb, qb_rows, nunits;
+  int nwk;          // split form: waves sharing each query tile's rows (each takes one 32-key half of every tile)
   int n_slots;      // cache rows when slot is set
   int stream_grid;  // stream form: ranges of the cut (one per CU, or a whole number per unit)
   int rpu;          // stream form: ranges per unit when the grid is a whole number of them per unit, else 0
@@ -87,8 +88,13 @@ __device__ __forceinline__ int unit_tile_lo(const AttnDev& a, int qb) { return (
 // Why sequence b is skipped (SVT_OK: it is not): its tree status, a cache
 // row outside the pool, or lengths outside 0 <= len <= lmax <= lmax_bound.
 __device__ __forceinline__ int seq_code(const AttnDev& a, int b, int lmax, int L) {
-  const int st = a.status ? a.status[b] : SVT_OK;
-  const int row = a.slot ? a.slot[b] : b;
+  // the optional arrays are read through a pointer that is never null (len
+  // when they are absent), so the loads need no branch and go out together
+  // with the lengths'
+  const int st0 = (a.status ? a.status : a.len)[b];
+  const int row0 = (a.slot ? a.slot : a.len)[b];
+  const int st = a.status ? st0 : SVT_OK;
+  const int row = a.slot ? row0 : b;
   if (st != SVT_OK) return st;
   if (row < 0 || row >= a.n_slots) return SVT_ERR_ARG;
   return (lmax >= 0 && lmax <= a.lmax_bound && L >= 0 && L <= lmax) ? SVT_OK : SVT_ERR_LENGTH;
@@ -105,7 +111,8 @@ struct WgCtx {
   int n_ptiles, n_ttiles;
 };
 
-__device__ __forceinline__ bool decode_wg(const AttnDev& a, WgCtx& c) {
+// Workgroup coordinates, from the workgroup id alone (no memory access).
+__device__ __forceinline__ bool decode_coords(const AttnDev& a, WgCtx& c) {
   // A unit is one (split, sequence, KV head); units are numbered with the
   // split slowest, so the full-size first splits are dispatched before the
   // ragged last ones.  The hardware sends workgroup id w to XCD w % 8: the
@@ -120,10 +127,17 @@ __device__ __forceinline__ bool decode_wg(const AttnDev& a, WgCtx& c) {
   c.g = unit % a.Hkv;
   c.b = (unit / a.Hkv) % a.B;
   c.split = unit / (a.Hkv * a.B);
+  return true;
+}
+
+// The sequence's lengths and status, and the key ranges of this split;
+// false when the sequence uses fewer splits.
+__device__ __forceinline__ bool decode_lengths(const AttnDev& a, WgCtx& c) {
   c.lmax = *a.lmax;
   c.L = a.len[c.b];
   c.code = seq_code(a, c.b, c.lmax, c.L);
-  c.cg = (int64_t)(c.code == SVT_OK ? (a.slot ? a.slot[c.b] : c.b) : 0) * a.Hkv + c.g;
+  const int row_v = (a.slot ? a.slot : a.len)[c.b];  // the load seq_code made
+  c.cg = (int64_t)(c.code == SVT_OK ? (a.slot ? row_v : c.b) : 0) * a.Hkv + c.g;
   c.ns_b = c.code == SVT_OK ? max(1, (c.L + a.kc - 1) / a.kc) : 1;
   if (c.split >= c.ns_b) return false;
   c.k_beg = c.split * a.kc;
@@ -249,19 +263,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
   __shared__ uint64_t maskw[kMaxQbRows * 4];
 
   WgCtx c;
-  if (!decode_wg(a, c)) return;
-  write_seq_status(a, c);
-  if (c.code != SVT_OK) {
-    if (c.split == 0) write_zero_rows<__bf16>(a, c, D);
-    return;
-  }
+  if (!decode_coords(a, c)) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave branches scalar
   const int lane = tid & 63;
   const int n16 = lane & 15;  // row/col inside a 16x16 tile
   const int grp = lane >> 4;  // lane group 0..3
-  const int nwk = (a.qb_rows == 32) ? 2 : 1;  // 2 waves share the rows when the block has 2 tiles
+  const int nwk = a.nwk;  // 2: a pair of waves shares the rows, one 32-key half of every tile each
   const int wq = wave / nwk, wk = wave % nwk;
 
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
@@ -271,6 +280,37 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
   const uint16_t* __restrict__ vtr = static_cast<const uint16_t*>(a.vtree);
   const int64_t bg = (int64_t)c.b * a.Hkv + c.g;
   const int r0 = c.qb * a.qb_rows;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query row n16 of
+  // each of its tiles, dims ks*32 + 8*grp .. +7.  Their addresses need no
+  // lengths, so they are requested before the lengths are read.
+  bf16x8 qf[QW][NKS];
+  int row_node[QW];  // node index of this lane's query row, -1 if padding
+  int row_head[QW];
+#pragma unroll
+  for (int t = 0; t < QW; ++t) {
+    const int r = r0 + (wq * QW + t) * 16 + n16;
+    const bool ok = r < a.R;
+    row_node[t] = ok ? r % a.T : -1;
+    row_head[t] = ok ? c.g * a.G + r / a.T : 0;
+    const uint16_t* qrow = q + (((int64_t)c.b * a.T + (ok ? row_node[t] : 0)) * a.Hq + row_head[t]) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ok) {
+        qf[t][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[t][ks][e] = (__bf16)0.0f;
+      }
+    }
+  }
+
+  if (!decode_lengths(a, c)) return;
+  write_seq_status(a, c);
+  if (c.code != SVT_OK) {
+    if (c.split == 0) write_zero_rows<__bf16>(a, c, D);
+    return;
+  }
 
   const int n_tiles = c.n_ptiles + c.n_ttiles;
   const int pad = c.lmax - c.L;
@@ -319,35 +359,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
     }
   };
 
-  // The first tiles' copies are issued before the Q fragments and mask
-  // words are loaded, so the two travel together (the wait for Q below also
-  // covers the copies: completion is counted in issue order).
+  // The first tiles' copies travel with the Q fragments (the wait for Q
+  // below also covers them: completion is counted in issue order).
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st)
     if (st < n_tiles) issue_tile(st, st);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query row n16 of
-  // each of its tiles, dims ks*32 + 8*grp .. +7.
-  bf16x8 qf[QW][NKS];
-  int row_node[QW];  // node index of this lane's query row, -1 if padding
-  int row_head[QW];
-#pragma unroll
-  for (int t = 0; t < QW; ++t) {
-    const int r = r0 + (wq * QW + t) * 16 + n16;
-    const bool ok = r < a.R;
-    row_node[t] = ok ? r % a.T : -1;
-    row_head[t] = ok ? c.g * a.G + r / a.T : 0;
-    const uint16_t* qrow = q + (((int64_t)c.b * a.T + (ok ? row_node[t] : 0)) * a.Hq + row_head[t]) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (ok) {
-        qf[t][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + grp * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[t][ks][e] = (__bf16)0.0f;
-      }
-    }
-  }
   bool tile_live[QW];  // does the tile hold any real row?  (wave-uniform)
 #pragma unroll
   for (int t = 0; t < QW; ++t) tile_live[t] = r0 + (wq * QW + t) * 16 < a.R;
@@ -1344,25 +1361,26 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
 }
 
 // --------------------------------------------------------------------------
-// fp32 VALU kernel: 64 query rows per workgroup, 16 per wave.
+// fp32 VALU kernel: one query row per wave, four per workgroup.
 // --------------------------------------------------------------------------
-// Each wave runs its rows one after another (a chain of dependent LDS reads
-// per row), so few rows per wave and more workgroups keep the latency down.
-constexpr int kFp32RowsPerWave = 4;
+// A row is a chain of dependent LDS reads (q . k, then P V, per key tile), so
+// one row per wave and more workgroups keep the call short: B=1 fp32 (36
+// rows, 137 keys) 21.6 -> 8.6 us against four rows per wave.
+constexpr int kFp32RowsPerWave = 1;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
   constexpr int DPL = D / 64;  // dims per lane
   constexpr int KS = D + 1;    // padded K row (floats) against bank conflicts
   constexpr int RPW = kFp32RowsPerWave;  // query rows per wave, handled one after another
-  __shared__ float qs[4 * RPW * D];
+  __shared__ __attribute__((aligned(16))) float qs[4 * RPW * D];
   __shared__ float ks[KT * KS];
   __shared__ float vs[KT * D];
-  __shared__ float ps[4][KT];
+  __shared__ __attribute__((aligned(16))) float ps[4][KT];
   __shared__ uint64_t mws[4 * RPW][4];
 
   WgCtx c;
-  if (!decode_wg(a, c)) return;
+  if (!decode_coords(a, c) || !decode_lengths(a, c)) return;
   write_seq_status(a, c);
   if (c.code != SVT_OK) {
     if (c.split == 0) write_zero_rows<float>(a, c, D);
@@ -1422,17 +1440,19 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
       const int rr = tid / 4, w = tid % 4, r = r0 + rr;
       if (r < a.R && w < a.W) mv = a.mask[((int64_t)c.b * a.T + r % a.T) * a.W + w];
     }
-    constexpr int NQ4 = 4 * RPW * D / 4 / 256;  // float4 of Q per thread
+    constexpr int NQF4 = RPW * D;                // float4 of the block's Q rows (4 * RPW rows)
+    constexpr int NQ4 = (NQF4 + 255) / 256;      // per thread
     float4 qr[NQ4];
 #pragma unroll
     for (int j = 0; j < NQ4; ++j) {
       const int x = 4 * (tid + 256 * j), rr = x / D, d = x % D, r = r0 + rr;
-      qr[j] = r < a.R ? *reinterpret_cast<const float4*>(
-                            q + (((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D + d)
-                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      qr[j] = (tid + 256 * j < NQF4 && r < a.R)
+                  ? *reinterpret_cast<const float4*>(q + (((int64_t)c.b * a.T + r % a.T) * a.Hq + c.g * a.G + r / a.T) * D + d)
+                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
-    for (int j = 0; j < NQ4; ++j) *reinterpret_cast<float4*>(qs + 4 * (tid + 256 * j)) = qr[j];
+    for (int j = 0; j < NQ4; ++j)
+      if (tid + 256 * j < NQF4) *reinterpret_cast<float4*>(qs + 4 * (tid + 256 * j)) = qr[j];
     if (c.n_ttiles > 0 && tid < 4 * RPW * 4) mws[tid / 4][tid % 4] = mv;
   }
   float m_run[RPW], l_run[RPW], o[RPW][DPL];
@@ -1471,8 +1491,20 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
         const uint64_t mw = mws[rr][t - c.n_ptiles];
         ok = ok && ((mw >> lane) & 1ull);
       }
-      float s = 0.0f;
-      for (int d = 0; d < D; ++d) s += qs[rr * D + d] * ks[lane * KS + d];
+      // q . k in four interleaved partial sums (a quarter of the dependent
+      // chain); the Q row is read four floats at a time (an LDS broadcast)
+      const float* qp = qs + rr * D;
+      const float* kp = ks + lane * KS;
+      float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int d = 0; d < D; d += 4) {
+        const float4 qv = *reinterpret_cast<const float4*>(qp + d);
+        s4[0] = fmaf(qv.x, kp[d], s4[0]);
+        s4[1] = fmaf(qv.y, kp[d + 1], s4[1]);
+        s4[2] = fmaf(qv.z, kp[d + 2], s4[2]);
+        s4[3] = fmaf(qv.w, kp[d + 3], s4[3]);
+      }
+      const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       const float x = ok ? s * a.scale_log2 : kNegInf;
       float tmax = x;
       for (int off = 32; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
@@ -1487,10 +1519,17 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
       ps[wave][lane] = p;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        float acc = o[j][e] * alpha;
         const int d = lane + 64 * e;
-        for (int k = 0; k < KT; ++k) acc += ps[wave][k] * vs[k * D + d];
-        o[j][e] = acc;
+        float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < KT; k += 4) {
+          const float4 pv = *reinterpret_cast<const float4*>(&ps[wave][k]);
+          a4[0] = fmaf(pv.x, vs[k * D + d], a4[0]);
+          a4[1] = fmaf(pv.y, vs[(k + 1) * D + d], a4[1]);
+          a4[2] = fmaf(pv.z, vs[(k + 2) * D + d], a4[2]);
+          a4[3] = fmaf(pv.w, vs[(k + 3) * D + d], a4[3]);
+        }
+        o[j][e] = o[j][e] * alpha + ((a4[0] + a4[1]) + (a4[2] + a4[3]));
       }
     }
   }
@@ -1521,33 +1560,56 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
 template <int D, typename E>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
   constexpr int DPL = D / 64;
+  constexpr int KB = 8;
   const int b = blockIdx.z, g = blockIdx.y;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= a.R) return;
+  const int64_t base = ((int64_t)b * a.Hkv + g) * a.ns;
+  // The partials of the first KB splits are loaded together with the
+  // sequence's lengths (their slots exist whatever the lengths are; slots of
+  // splits the sequence does not use are loaded and ignored), so a call with
+  // at most KB splits pays one memory round trip before the merge.  The
+  // arithmetic runs in split order: the maximum, then the weighted sums.
+  float mv[KB], lv[KB], ov[KB][DPL];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    const int64_t pr = (base + min(j, a.ns - 1)) * a.R + r;
+    mv[j] = a.ws_ml[pr * 2];
+    lv[j] = a.ws_ml[pr * 2 + 1];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ov[j][e] = a.ws_o[pr * D + lane + 64 * e];
+  }
   const int lmax = *a.lmax;
   const int L = a.len[b];
   if (seq_code(a, b, lmax, L) != SVT_OK) return;
   const int ns_b = max(1, (L + a.kc - 1) / a.kc);
   if (ns_b <= 1) return;
-  const int64_t base = ((int64_t)b * a.Hkv + g) * a.ns;
-  // The loads of KB splits are issued before any of them is used, so a
-  // merge pays few memory round trips; the arithmetic runs in split order.
-  constexpr int KB = 8;
+  const int n0 = min(ns_b, KB);
   float mx = kNegInf;
-  for (int s0 = 0; s0 < ns_b; s0 += KB) {
-    float mv[KB];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) mv[j] = s0 + j < ns_b ? a.ws_ml[((base + s0 + j) * a.R + r) * 2] : kNegInf;
+  for (int j = 0; j < KB; ++j)
+    if (j < n0) mx = fmaxf(mx, mv[j]);
+  for (int s0 = KB; s0 < ns_b; s0 += KB) {
+    float mw[KB];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) mx = fmaxf(mx, mv[j]);
+    for (int j = 0; j < KB; ++j) mw[j] = s0 + j < ns_b ? a.ws_ml[((base + s0 + j) * a.R + r) * 2] : kNegInf;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) mx = fmaxf(mx, mw[j]);
   }
   const float mu = mx == kNegInf ? 0.0f : mx;
   float lsum = 0.0f, acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  for (int s0 = 0; s0 < ns_b; s0 += KB) {
-    float mv[KB], lv[KB], ov[KB][DPL];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    if (j >= n0) break;
+    const float w = exp2f(mv[j] - mu);
+    lsum += lv[j] * w;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += ov[j][e] * w;
+  }
+  for (int s0 = KB; s0 < ns_b; s0 += KB) {
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int64_t pr = (base + min(s0 + j, ns_b - 1)) * a.R + r;
@@ -1742,6 +1804,7 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.ns = p.ns;
   d.nqb = p.nqb;
   d.qb_rows = p.qb_rows;
+  d.nwk = p.nwk;
   d.nqt = p.nqt;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   d.scale_log2 = scale * kLog2e;
