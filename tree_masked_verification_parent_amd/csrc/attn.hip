@@ -1275,6 +1275,59 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int* pref = a.ws_pref;
   const int* npref = a.ws_pref + a.B + 1;
+  if (a.rpu > 0) {
+    // One sequence, a whole number of ranges per unit: when every range
+    // holds tiles of the unit, unit u's pieces are ranges u * rpu ..
+    // u * rpu + rpu - 1, each ending at its range's end (slot 2c + 1), so no
+    // piece list is needed, and the first batch of partials is requested
+    // together with the sequence's tile count (its slots exist in any case).
+    const int rl = blockIdx.y * RPW + threadIdx.x / TPR;
+    const int d0 = (threadIdx.x % TPR) * DPT;
+    const int t0 = unit_tile_lo(a, qb);
+    const int r = 16 * t0 + rl;
+    if (!(rl < 16 * (unit_tile_lo(a, qb + 1) - t0) && r < a.R)) return;
+    const int np = a.rpu;
+    const int64_t slot0 = 2 * (int64_t)u * np + 1;
+    float mi[KB], li[KB], si[KB];
+    float oi[KB][DPT];
+    auto load_batch = [&](int k) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int64_t pr = (slot0 + 2 * (int64_t)min(k + j, np - 1)) * a.qb_rows + rl;
+        const float4 mls = a.ws_mls[pr];
+        mi[j] = mls.x;
+        li[j] = mls.y;
+        si[j] = mls.z;
+        typedef _Float16 f16xN __attribute__((ext_vector_type(DPT)));
+        const f16xN v = *reinterpret_cast<const f16xN*>(a.ws_h + pr * D + d0);
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) oi[j][e] = (float)v[e];
+      }
+    };
+    load_batch(0);
+    const int ntl1 = pref[b + 1] - pref[b];
+    if (ntl1 == 0) return;  // the sequence was skipped: no partials, zeros are written
+    const int PC1 = a.piece_cost;
+    if ((ntl1 + PC1) / np >= PC1 + 2) {  // every range holds at least one tile of the unit
+      float mx = kNegInf, l = 0.0f;
+      float acc[DPT];
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) acc[e] = 0.0f;
+      for (int k = 0; k < np; k += KB) {
+        if (k > 0) load_batch(k);
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          if (k + j >= np) break;
+          merge_piece(mx, l, acc, mi[j], li[j], si[j], oi[j]);
+        }
+      }
+      const float inv = 1.0f / l;
+      __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) orow[d0 + e] = (__bf16)(acc[e] * inv);
+      return;
+    }
+  }
   const int ntl = pref[b + 1] - pref[b];
   if (ntl == 0) return;
   const int UPB = a.Hkv * a.nqb;
