@@ -348,6 +348,10 @@ ATTN_CASES = [
      [1 + (53 * i) % 700 for i in range(32)]),
     ("bf16-d64-b32-12tiles", dict(B=32, dtype="bf16", Hq=32, Hkv=8, D=64, M=44),
      [(71 * i) % 650 for i in range(31)] + [650]),
+    # one sequence long enough that every range of its whole-ranges-per-unit
+    # grid holds tiles: the stream combine takes the pieces without a list
+    ("bf16-d128-b1-wholeranges", dict(B=1, dtype="bf16", Hq=8, Hkv=8, D=128, M=127), [8200]),
+    ("bf16-d64-b1-wholeranges", dict(B=1, dtype="bf16", Hq=16, Hkv=4, D=64, M=31), [17000]),
 ]
 
 
