@@ -50,6 +50,20 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int KT = 64;  // keys per LDS tile
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, base-2 units
 
+// Stream form: what the combine needs about the unit that range c's last
+// piece belongs to, when range c is the first of several ranges holding that
+// unit's tiles (the main kernel's workgroup for range c writes it).
+struct RangeMeta {
+  int u;    // the unit (b * Hkv * nqb + g * nqb + qb), or -1: no unit starts a cut in range c
+  int c1;   // last range holding tiles of the unit
+  int ntl;  // key tiles of the unit
+  int pad0;
+  int64_t cu;     // cost position of the unit's set-up
+  int64_t p;      // stream position of the unit's first tile
+  int64_t ct;     // total cost of the stream
+  int64_t pad;
+};
+
 struct AttnDev {
   const void* q;
   const void* kcache;
@@ -68,6 +82,7 @@ struct AttnDev {
   _Float16* ws_h;  // stream form: partial O / l per row, divided by the row's scale s, [2*grid][qb_rows][D]
   float4* ws_mls;  // stream form: (m, l, s, 0) per partial row
   int* ws_pref;  // stream form: tiles before each sequence [B + 1], then non-empty sequences before it [B + 1]
+  RangeMeta* ws_meta;  // stream form: one per range
   int64_t cap;
   int B, T, Hq, Hkv, G, R, W;
   int lmax_bound, kc, ns, nqb, qb_rows, nunits;
@@ -639,9 +654,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnDev a) {
 // up a compute wave, and the compute waves' own loads (Q, mask words) never
 // wait behind tile copies.  A unit lying wholly inside
 // one range is normalised and written directly; a unit cut by range ends
-// leaves (m, l, O) partials in two slots per workgroup (slot 2c: a piece that
-// ends at its unit's end, slot 2c+1: the piece that ends at the range end), and
-// attn_stream_combine_kernel merges them in stream order.  No workgroup waits
+// leaves (m, l, O) partials in two slots per range c (slot 2c + 1: the
+// range's last piece when its unit goes on past the range end; slot 2c: the
+// range's first piece when it continues a unit from an earlier range and
+// ends with it), and attn_stream_combine_kernel merges them in stream order.  No workgroup waits
 // for another, and the result does not depend on timing.
 // --------------------------------------------------------------------------
 constexpr int kStreamMaxB = kStreamMaxBatch;
@@ -686,15 +702,13 @@ __device__ __forceinline__ UnitCut unit_cut(int64_t ct, int64_t cu, int64_t p, i
 }
 // Whether range cc (c0 <= cc <= c1) holds a piece of the unit (ranges between
 // c0 and c1 may be empty when there are fewer tiles than ranges), and the
-// partial slot that piece leaves: 2cc + 1 when it ends at the range's end,
-// 2cc when it ends at the unit's end inside the range.  The last range ends
-// at the unit's end exactly when its cost end reaches no further than the
-// next unit's first tile.
+// partial slot that piece leaves: 2cc + 1 when the unit goes on past the
+// range (cc < c1), 2cc for its last piece (range c1).
 __device__ __forceinline__ bool unit_piece(const UnitCut& u, int cc, int* slot) {
   const int64_t clo = stream_lo(cc, u.ct, u.g), chi = stream_lo(cc + 1, u.ct, u.g);
   const int64_t tlo = cc == u.c0 ? u.p : u.p + (clo - u.cu - u.pc);
   const int64_t thi = cc < u.c1 ? u.p + (chi - u.cu - u.pc) : u.p + u.ntl;
-  *slot = 2 * cc + ((cc < u.c1 || chi <= u.cu + u.ntl + 2 * (int64_t)u.pc) ? 1 : 0);
+  *slot = 2 * cc + (cc < u.c1 ? 1 : 0);
   return tlo < thi;
 }
 
@@ -755,50 +769,89 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
   const bool lag = kLagging && wave < NW && ((wave >> 2) & 1);
 
   // ---- per-sequence tile counts and their prefix (every workgroup computes it)
-  if (tid == 0) {
-    s_pref[0] = 0;
-    s_npref[0] = 0;
-    s_carry = 0;
-    s_carry2 = 0;
-  }
-  __syncthreads();
-  for (int base = 0; base < B; base += NT) {
-    const int b = base + tid;
-    int v = 0, code;
+  // With at most 64 sequences every wave holds the table in registers (lane
+  // b: sequence b) and finds its range bounds and first unit with wave
+  // ballots, so the first copies wait for one round of loads and no barrier;
+  // wave 0 also stores the table in LDS for the walk through the range.
+  // Larger batches build it in LDS with a workgroup-wide scan.
+  const bool small_b = B <= 64;
+  int rv = 0, rx = 0, rx2 = 0, rL = 0, rrow = 0;  // small batch, lane b: tiles, inclusive prefixes, length, cache row
+  if (small_b) {
+    const int b = lane;
+    int code;
     if (b < B) {
-      v = stream_seq_tiles(a, b, lmax, &code);
-      s_len[b] = a.len[b];
-      s_row[b] = a.slot ? a.slot[b] : b;
+      rv = stream_seq_tiles(a, b, lmax, &code);
+      rL = a.len[b];
+      rrow = a.slot ? a.slot[b] : b;
     }
-    int x = v, x2 = v > 0 ? 1 : 0;
+    rx = rv;
+    rx2 = rv > 0 ? 1 : 0;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o), y2 = __shfl_up(x2, o);
+      const int y = __shfl_up(rx, o), y2 = __shfl_up(rx2, o);
       if (lane >= o) {
-        x += y;
-        x2 += y2;
+        rx += y;
+        rx2 += y2;
       }
     }
-    if (lane == 63) {
-      s_wsum[wave] = x;
-      s_wsum2[wave] = x2;
+    if (wave == 0) {
+      if (b < B) {
+        s_pref[b + 1] = rx;
+        s_npref[b + 1] = rx2;
+        s_len[b] = rL;
+        s_row[b] = rrow;
+      }
+      if (lane == 0) {
+        s_pref[0] = 0;
+        s_npref[0] = 0;
+      }
+    }
+  } else {
+    if (tid == 0) {
+      s_pref[0] = 0;
+      s_npref[0] = 0;
+      s_carry = 0;
+      s_carry2 = 0;
     }
     __syncthreads();
-    int off = s_carry, off2 = s_carry2;
-    for (int w = 0; w < wave; ++w) {
-      off += s_wsum[w];
-      off2 += s_wsum2[w];
+    for (int base = 0; base < B; base += NT) {
+      const int b = base + tid;
+      int v = 0, code;
+      if (b < B) {
+        v = stream_seq_tiles(a, b, lmax, &code);
+        s_len[b] = a.len[b];
+        s_row[b] = a.slot ? a.slot[b] : b;
+      }
+      int x = v, x2 = v > 0 ? 1 : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o), y2 = __shfl_up(x2, o);
+        if (lane >= o) {
+          x += y;
+          x2 += y2;
+        }
+      }
+      if (lane == 63) {
+        s_wsum[wave] = x;
+        s_wsum2[wave] = x2;
+      }
+      __syncthreads();
+      int off = s_carry, off2 = s_carry2;
+      for (int w = 0; w < wave; ++w) {
+        off += s_wsum[w];
+        off2 += s_wsum2[w];
+      }
+      if (b < B) {
+        s_pref[b + 1] = off + x;
+        s_npref[b + 1] = off2 + x2;
+      }
+      __syncthreads();
+      if (tid == NT - 1) {
+        s_carry = off + x;
+        s_carry2 = off2 + x2;
+      }
+      __syncthreads();
     }
-    if (b < B) {
-      s_pref[b + 1] = off + x;
-      s_npref[b + 1] = off2 + x2;
-    }
-    __syncthreads();
-    if (tid == NT - 1) {
-      s_carry = off + x;
-      s_carry2 = off2 + x2;
-    }
-    __syncthreads();
   }
   const int G = a.stream_grid;  // ranges of the cut; workgroups past them (if any) get none
   // Consecutive ranges go to one XCD (the hardware sends workgroup w to XCD
@@ -815,33 +868,85 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     c = (g * a.nqb + qb) * a.rpu + r;
   }
   const int UPB = a.Hkv * a.nqb;  // units per sequence
-  const int64_t N = (int64_t)UPB * s_pref[B];
+  // tiles and non-empty sequences of the whole batch
+  const int tot_t = small_b ? __builtin_amdgcn_readlane(rx, 63) : s_pref[B];
+  const int tot_n = small_b ? __builtin_amdgcn_readlane(rx2, 63) : s_npref[B];
+  const int64_t N = (int64_t)UPB * tot_t;
   // Ranges are equal in cost, not in tiles: a unit costs its key tiles plus
   // piece_cost for its set-up and output, so a range that starts several
   // units gets fewer tiles.  Cost position p maps to the stream tile it
   // reaches (positions inside a unit's set-up map to its first tile).
   const int PC = a.piece_cost;
   auto seq_cost = [&](int b) { return (int64_t)UPB * ((int64_t)s_pref[b] + (int64_t)PC * s_npref[b]); };
-  const int64_t CT = seq_cost(B);
+  const int64_t CT = (int64_t)UPB * ((int64_t)tot_t + (int64_t)PC * tot_n);
+  // The last sequence l whose cost, or (by_tile) whose first stream tile, is
+  // at most p, with its tiles before it, non-empty sequences before it and
+  // tile count; never an empty sequence (the next one starts at the same
+  // position).  Small batch: one ballot over the lanes; otherwise a binary
+  // search of the LDS table.
+  struct SeqAt {
+    int l, pref, npref, ntl;
+  };
+  auto seq_at = [&](int64_t p, bool by_tile) -> SeqAt {
+    SeqAt r;
+    if (small_b) {
+      const int pe = rx - rv, pe2 = rx2 - (rv > 0 ? 1 : 0);  // this lane's exclusive prefixes
+      const int64_t key = (int64_t)UPB * (by_tile ? (int64_t)pe : (int64_t)pe + (int64_t)PC * pe2);
+      const uint64_t m = __ballot(lane < B && key <= p);  // lane 0 always qualifies (p >= 0)
+      r.l = 63 - __builtin_clzll(m);
+      r.pref = __builtin_amdgcn_readlane(pe, r.l);
+      r.npref = __builtin_amdgcn_readlane(pe2, r.l);
+      r.ntl = __builtin_amdgcn_readlane(rv, r.l);
+    } else {
+      int l = 0, h = B;
+      while (h - l > 1) {
+        const int m = (l + h) >> 1;
+        if ((by_tile ? (int64_t)UPB * s_pref[m] : seq_cost(m)) <= p) l = m;
+        else h = m;
+      }
+      r.l = __builtin_amdgcn_readfirstlane(l);
+      r.pref = __builtin_amdgcn_readfirstlane(s_pref[r.l]);
+      r.npref = __builtin_amdgcn_readfirstlane(s_npref[r.l]);
+      r.ntl = __builtin_amdgcn_readfirstlane(s_pref[r.l + 1]) - r.pref;
+    }
+    return r;
+  };
   auto cost_to_tile = [&](int64_t p) -> int64_t {
     if (p >= CT) return N;
-    int l = 0, h = B;
-    while (h - l > 1) {
-      const int m = (l + h) >> 1;
-      if (seq_cost(m) <= p) l = m;
-      else h = m;
-    }
-    const int ntl = s_pref[l + 1] - s_pref[l];
-    const int off = (int)(p - seq_cost(l));
-    const int j = off / (ntl + PC), r = off - j * (ntl + PC);
-    return (int64_t)UPB * s_pref[l] + (int64_t)j * ntl + max(0, r - PC);
+    const SeqAt q = seq_at(p, false);
+    const int off = (int)(p - (int64_t)UPB * ((int64_t)q.pref + (int64_t)PC * q.npref));
+    const int j = off / (q.ntl + PC), r = off - j * (q.ntl + PC);
+    return (int64_t)UPB * q.pref + (int64_t)j * q.ntl + max(0, r - PC);
   };
   const int64_t lo = cost_to_tile(stream_lo(c, CT, G)), hi = cost_to_tile(stream_lo(c + 1, CT, G));
-  if (c == 0 && a.ws_pref)
-    for (int b = tid; b <= B; b += NT) {
-      a.ws_pref[b] = s_pref[b];
-      a.ws_pref[B + 1 + b] = s_npref[b];
+  // The combine's record of this range: when the range ends inside a unit
+  // whose first tile it holds, the unit and the ranges of its pieces, so
+  // that the combine needs no prefix table to find them.  Wave 0 computes it
+  // (the small-batch search is a ballot over its lanes) before its first
+  // loads; lane 0 stores it.
+  // Not needed when the combine finds the pieces without it: one sequence,
+  // a whole number of ranges per unit, every range holding tiles of its unit
+  // (the combine's test, on the same numbers).
+  const bool need_meta = a.ws_meta && c < G && !(a.rpu > 0 && tot_t > 0 && (tot_t + PC) / a.rpu >= PC + 2);
+  auto range_meta = [&]() {
+    RangeMeta m{-1, 0, 0, 0, 0, 0, 0, 0};
+    if (lo < hi) {
+      const SeqAt q = seq_at(hi - 1, true);  // the sequence of the range's last tile
+      const int64_t sb = (int64_t)UPB * q.pref;
+      const int j = (int)div_floor(hi - 1 - sb, q.ntl);
+      const int64_t base = sb + (int64_t)j * q.ntl;
+      if (hi < base + q.ntl) {
+        const int64_t cu = (int64_t)UPB * ((int64_t)q.pref + (int64_t)PC * q.npref) + (int64_t)j * (q.ntl + PC);
+        const UnitCut uc = unit_cut(CT, cu, base, G, PC, q.ntl);
+        if (uc.c0 == c && uc.c1 > c) m = RangeMeta{q.l * UPB + j, uc.c1, q.ntl, 0, cu, base, CT, 0};
+      }
     }
+    return m;
+  };
+  if (wave == 0 && need_meta) {
+    const RangeMeta m = range_meta();
+    if (lane == 0) a.ws_meta[c] = m;
+  }
 
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.kcache);
@@ -858,30 +963,31 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     int64_t base;
     const uint16_t *kp, *vp, *kt, *vt;  // prefix content start, tree rows
   };
-  auto fill = [&](Cur& r) {
-    r.L = __builtin_amdgcn_readfirstlane(s_len[r.b]);
+  auto fill_lr = [&](Cur& r, int L, int row) {
+    r.L = L;
     r.np = (r.L + KT - 1) / KT;
     const int64_t bg = (int64_t)r.b * a.Hkv + r.j / a.nqb;
-    const int64_t cg = (int64_t)__builtin_amdgcn_readfirstlane(s_row[r.b]) * a.Hkv + r.j / a.nqb;
+    const int64_t cg = (int64_t)row * a.Hkv + r.j / a.nqb;
     r.kp = kc + (cg * a.cap + (lmax - r.L)) * D;
     r.vp = vc + (cg * a.cap + (lmax - r.L)) * D;
     r.kt = ktr + bg * a.T * D;
     r.vt = vtr + bg * a.T * D;
   };
+  auto fill = [&](Cur& r) {
+    fill_lr(r, __builtin_amdgcn_readfirstlane(s_len[r.b]), __builtin_amdgcn_readfirstlane(s_row[r.b]));
+  };
+  // The unit holding stream tile x (small batch: the sequence's length and
+  // cache row come from the lanes, not from LDS).
   auto locate = [&](int64_t x) {
-    int l = 0, h = B;
-    while (h - l > 1) {
-      const int m = (l + h) >> 1;
-      if ((int64_t)UPB * s_pref[m] <= x) l = m;
-      else h = m;
-    }
+    const SeqAt q = seq_at(x, true);
     Cur r;
-    r.b = __builtin_amdgcn_readfirstlane(l);
-    r.ntl = __builtin_amdgcn_readfirstlane(s_pref[r.b + 1] - s_pref[r.b]);
-    const int64_t sb = (int64_t)UPB * s_pref[r.b];
-    r.j = (int)((x - sb) / r.ntl);
+    r.b = q.l;
+    r.ntl = q.ntl;
+    const int64_t sb = (int64_t)UPB * q.pref;
+    r.j = (int)div_floor(x - sb, r.ntl);
     r.base = sb + (int64_t)r.j * r.ntl;
-    fill(r);
+    if (small_b) fill_lr(r, __builtin_amdgcn_readlane(rL, r.b), __builtin_amdgcn_readlane(rrow, r.b));
+    else fill(r);
     return r;
   };
   auto advance = [&](Cur& r) {
@@ -958,6 +1064,12 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     cur = locate(lo);
     pcur = cur;
   }
+  if (small_b) __syncthreads();  // wave 0's LDS table, read from here on
+  if (c == 0 && a.ws_pref)
+    for (int b = tid; b <= B; b += NT) {
+      a.ws_pref[b] = s_pref[b];
+      a.ws_pref[B + 1 + b] = s_npref[b];
+    }
   // Producer cursor: pcur/px walk the range ahead of the compute waves.
   int64_t px = lo;
   auto produce = [&](int st) {
@@ -1113,6 +1225,7 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
     }
   };
 
+
   if (wave >= NW) {
     // Producer of K: three tiles ahead.  Before barrier y it waits for its
     // copies of tile y (tiles y + 1 and y + 2 may still be in flight); after
@@ -1222,7 +1335,7 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
           *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * grp) = v;
         }
       } else {
-        const int slot = 2 * c + (pend == hi ? 1 : 0);
+        const int slot = 2 * c + ((pend == hi && pend < cur.base + cur.ntl) ? 1 : 0);
         const int64_t pr = (int64_t)slot * a.qb_rows + lt * 16 + n16;
         const float l = lacc[qt][0];
         const float s_row = l > 0.0f ? pscale[qt] / l : 0.0f;      // max |O / l| of the row
@@ -1258,11 +1371,16 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
 }
 
 // Merges the partials of the units that range ends cut, in stream order.
-// Grid (unit, group of rows): D / DPT threads per row, DPT dims each (the
-// launch picks DPT so that the grid covers the chip).  The first wave lists
-// the unit's pieces (their partial slots, empty ranges skipped) in LDS, one
-// range per lane; the partials of KB = 32 / DPT pieces are loaded before any
-// of them is merged.  Units inside a single range return at once.
+// Grid (range, group of rows): D / DPT threads per row, DPT dims each (the
+// launch picks DPT so that the grid covers the chip).  A cut unit is merged by
+// the workgroups of the first range holding its tiles.  That range's record
+// (written by the main kernel) names the unit and its last range; it is loaded together with the partials of the two
+// pieces of a unit cut once (slots 2c + 1 and 2c + 2), so such a unit costs
+// one memory round trip.  A
+// unit spread over more ranges lists the rest of its pieces (empty ranges
+// skipped) in LDS, one range per lane, and merges them in batches of
+// KB = 32 / DPT pieces.  With a whole number of ranges per unit (one
+// sequence) the pieces are known without the record: see below.
 constexpr int kMaxPieces = 64;  // pieces listed per pass (one wave)
 
 template <int D, int DPT>
@@ -1270,45 +1388,76 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   constexpr int TPR = D / DPT;   // threads per row
   constexpr int RPW = 256 / TPR; // rows per workgroup
   constexpr int KB = 32 / DPT;  // pieces loaded per batch
-  const int u = blockIdx.x;
-  const int qb = u % a.nqb, bg = u / a.nqb;
-  const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int* pref = a.ws_pref;
-  const int* npref = a.ws_pref + a.B + 1;
+  typedef _Float16 f16xN __attribute__((ext_vector_type(DPT)));
+  int cr = blockIdx.x;  // range (with a whole number of ranges per unit: the unit)
+  const int G = a.stream_grid;
+  const int rl = blockIdx.y * RPW + threadIdx.x / TPR;
+  const int d0 = (threadIdx.x % TPR) * DPT;
+  const int rld = min(rl, a.qb_rows - 1);  // row the loads use (in the slot whatever rl is)
+  // Row rld of partial slot `slot`: (m, l, s) and DPT dims of O / (l s).
+  auto load_piece = [&](int64_t slot, float& mi, float& li, float& si, float (&oi)[DPT]) {
+    const int64_t pr = slot * a.qb_rows + rld;
+    const float4 mls = a.ws_mls[pr];
+    mi = mls.x;
+    li = mls.y;
+    si = mls.z;
+    const f16xN v = *reinterpret_cast<const f16xN*>(a.ws_h + pr * D + d0);
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) oi[e] = (float)v[e];
+  };
+  // The unit's output row r of query block qb, or false for rows past it.
+  auto unit_row = [&](int u, int& b, int& g, int& r) {
+    const int qb = u % a.nqb, bg = u / a.nqb;
+    g = bg % a.Hkv;
+    b = bg / a.Hkv;
+    const int t0 = unit_tile_lo(a, qb);
+    r = 16 * t0 + rl;
+    return rl < 16 * (unit_tile_lo(a, qb + 1) - t0) && r < a.R;
+  };
+  auto store_row = [&](int b, int g, int r, const float (&acc)[DPT], float l) {
+    const float inv = 1.0f / l;
+    __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
+    if constexpr (DPT % 4 == 0) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int e = 0; e < DPT; e += 4) {
+        bf16x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (__bf16)(acc[e + k] * inv);
+        *reinterpret_cast<bf16x4*>(orow + d0 + e) = v;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) orow[d0 + e] = (__bf16)(acc[e] * inv);
+    }
+  };
+
   if (a.rpu > 0) {
     // One sequence, a whole number of ranges per unit: when every range
-    // holds tiles of the unit, unit u's pieces are ranges u * rpu ..
-    // u * rpu + rpu - 1, each ending at its range's end (slot 2c + 1), so no
-    // piece list is needed, and the first batch of partials is requested
-    // together with the sequence's tile count (its slots exist in any case).
-    const int rl = blockIdx.y * RPW + threadIdx.x / TPR;
-    const int d0 = (threadIdx.x % TPR) * DPT;
-    const int t0 = unit_tile_lo(a, qb);
-    const int r = 16 * t0 + rl;
-    if (!(rl < 16 * (unit_tile_lo(a, qb + 1) - t0) && r < a.R)) return;
+    // holds tiles of the unit, unit u's pieces are those of ranges u * rpu ..
+    // u * rpu + rpu - 1 (slot 2c + 1, the last one 2c), so the unit's
+    // workgroups merge them with no record and no list, the
+    // first batch of partials requested together with the sequence's tile
+    // count (its slots exist in any case).  The grid then has one workgroup
+    // per unit and group of rows.
     const int np = a.rpu;
-    const int64_t slot0 = 2 * (int64_t)u * np + 1;
+    const int u = cr;
     float mi[KB], li[KB], si[KB];
     float oi[KB][DPT];
     auto load_batch = [&](int k) {
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
-        const int64_t pr = (slot0 + 2 * (int64_t)min(k + j, np - 1)) * a.qb_rows + rl;
-        const float4 mls = a.ws_mls[pr];
-        mi[j] = mls.x;
-        li[j] = mls.y;
-        si[j] = mls.z;
-        typedef _Float16 f16xN __attribute__((ext_vector_type(DPT)));
-        const f16xN v = *reinterpret_cast<const f16xN*>(a.ws_h + pr * D + d0);
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) oi[j][e] = (float)v[e];
+        const int kk = min(k + j, np - 1);
+        load_piece(2 * ((int64_t)u * np + kk) + (kk < np - 1 ? 1 : 0), mi[j], li[j], si[j], oi[j]);
       }
     };
     load_batch(0);
-    const int ntl1 = pref[b + 1] - pref[b];
+    const int ntl1 = a.ws_pref[1] - a.ws_pref[0];
     if (ntl1 == 0) return;  // the sequence was skipped: no partials, zeros are written
     const int PC1 = a.piece_cost;
     if ((ntl1 + PC1) / np >= PC1 + 2) {  // every range holds at least one tile of the unit
+      int b, g, r;
+      if (!unit_row(u, b, g, r)) return;
       float mx = kNegInf, l = 0.0f;
       float acc[DPT];
 #pragma unroll
@@ -1321,47 +1470,53 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
           merge_piece(mx, l, acc, mi[j], li[j], si[j], oi[j]);
         }
       }
-      const float inv = 1.0f / l;
-      __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
-#pragma unroll
-      for (int e = 0; e < DPT; ++e) orow[d0 + e] = (__bf16)(acc[e] * inv);
+      store_row(b, g, r, acc, l);
       return;
     }
+    // Some ranges of the unit hold no tile (a short sequence): its pieces
+    // are found from the record of its first cut range, among its own ranges.
+    int c0 = -1;
+    for (int c = u * np; c < (u + 1) * np; ++c)
+      if (a.ws_meta[c].u == u) {
+        c0 = c;
+        break;
+      }
+    if (c0 < 0) return;  // the unit lies in one range: written directly
+    cr = c0;
   }
-  const int ntl = pref[b + 1] - pref[b];
-  if (ntl == 0) return;
-  const int UPB = a.Hkv * a.nqb;
-  const int G = a.stream_grid;
-  const int PC = a.piece_cost;
-  // The unit's cost interval is [CU, CU + PC + ntl): its set-up, then its
-  // tiles; the ranges are equal cuts of the total cost CT (as in the main
-  // kernel), and a range boundary at cost p inside the unit's tiles falls
-  // before tile P + (p - CU - PC).
-  const int64_t CT = (int64_t)UPB * ((int64_t)pref[a.B] + (int64_t)PC * npref[a.B]);
-  const int64_t CU = (int64_t)UPB * ((int64_t)pref[b] + (int64_t)PC * npref[b]) + (int64_t)(g * a.nqb + qb) * (ntl + PC);
-  const int64_t P = (int64_t)UPB * pref[b] + (int64_t)(g * a.nqb + qb) * ntl;
-  const UnitCut uc = unit_cut(CT, CU, P, G, PC, ntl);
-  const int c0 = uc.c0, c1 = uc.c1;
-  if (c0 == c1) return;
-  __shared__ int s_slot[kMaxPieces];
-  __shared__ int s_np;
-  const int rl = blockIdx.y * RPW + threadIdx.x / TPR;
-  const int d0 = (threadIdx.x % TPR) * DPT;
-  const int t0 = unit_tile_lo(a, qb);
-  const int r = 16 * t0 + rl;
-  const bool row_ok = rl < 16 * (unit_tile_lo(a, qb + 1) - t0) && r < a.R;
-  // Online merge in range order (deterministic); ranges between c0 and c1
-  // may be empty (fewer tiles than workgroups) and hold no piece.
+
+  // ---- the record of range cr, and the partials a unit cut once uses
+  const RangeMeta m = a.ws_meta[cr];
+  float m0, l0, s0, o0[DPT], m1, l1, s1, o1[DPT];
+  load_piece(2 * (int64_t)cr + 1, m0, l0, s0, o0);
+  load_piece(min(2 * (int64_t)cr + 2, 2 * (int64_t)G - 1), m1, l1, s1, o1);
+  if (m.u < 0) return;  // workgroup-uniform
+  int b, g, r;
+  const bool row_ok = unit_row(m.u, b, g, r);
+  // Online merge in range order (deterministic): this range's piece first.
   float mx = kNegInf, l = 0.0f;
   float acc[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) acc[e] = 0.0f;
-  for (int cs = c0; cs <= c1; cs += kMaxPieces) {
+  merge_piece(mx, l, acc, m0, l0, s0, o0);
+  if (m.c1 == cr + 1) {
+    if (!row_ok) return;
+    merge_piece(mx, l, acc, m1, l1, s1, o1);
+    store_row(b, g, r, acc, l);
+    return;
+  }
+  // ---- a unit over three or more ranges: list the pieces of ranges
+  // cr + 1 .. c1 (ranges between may be empty when there are fewer tiles than
+  // ranges) and merge them in batches
+  const UnitCut uc = unit_cut(m.ct, m.cu, m.p, G, a.piece_cost, m.ntl);
+  __shared__ int s_slot[kMaxPieces];
+  __shared__ int s_np;
+  for (int cs = cr + 1; cs <= m.c1; cs += kMaxPieces) {
     __syncthreads();
     if (threadIdx.x < kMaxPieces) {
       const int cc = cs + (int)threadIdx.x;
       int slot = 0;
-      const bool has = cc <= c1 && unit_piece(uc, cc, &slot);
+      const bool has = cc <= m.c1 && unit_piece(uc, cc, &slot);
       const uint64_t bal = __ballot(has);
       const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
       if (has) s_slot[below] = slot;
@@ -1373,21 +1528,10 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
     for (int k = 0; k < np; k += KB) {
       float mi[KB], li[KB], si[KB];
       float oi[KB][DPT];  // converted on load: the merge loop below indexes it
+      // every slot loads (past the last piece: the last piece again), so the
+      // batch's loads issue back to back; only the real pieces are merged
 #pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        // every slot loads (past the last piece: the last piece again), so the
-        // batch's loads issue back to back; only the real pieces are merged
-        const int64_t pr = (int64_t)s_slot[min(k + j, np - 1)] * a.qb_rows + rl;
-        const float4 mls = a.ws_mls[pr];
-        mi[j] = mls.x;
-        li[j] = mls.y;
-        si[j] = mls.z;
-        const _Float16* src = a.ws_h + pr * D + d0;
-        typedef _Float16 f16xN __attribute__((ext_vector_type(DPT)));
-        const f16xN v = *reinterpret_cast<const f16xN*>(src);
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) oi[j][e] = (float)v[e];
-      }
+      for (int j = 0; j < KB; ++j) load_piece(s_slot[min(k + j, np - 1)], mi[j], li[j], si[j], oi[j]);
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         if (k + j >= np) break;
@@ -1396,21 +1540,7 @@ __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
     }
   }
   if (!row_ok) return;
-  const float inv = 1.0f / l;
-  __bf16* orow = static_cast<__bf16*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
-  if constexpr (DPT % 4 == 0) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int e = 0; e < DPT; e += 4) {
-      bf16x4 v;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = (__bf16)(acc[e + k] * inv);
-      *reinterpret_cast<bf16x4*>(orow + d0 + e) = v;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) orow[d0 + e] = (__bf16)(acc[e] * inv);
-  }
+  store_row(b, g, r, acc, l);
 }
 
 // --------------------------------------------------------------------------
@@ -1701,6 +1831,11 @@ static int device_cu_count() {
   return n;
 }
 
+// Stream-form workspace: the prefix table, then the range records, then the
+// partials' (m, l, s) and their fp16 rows.
+static size_t stream_pref_bytes(int B) { return ((size_t)2 * (B + 1) * sizeof(int) + 255) / 256 * 256; }
+static size_t stream_meta_bytes(int grid) { return ((size_t)grid * sizeof(RangeMeta) + 255) / 256 * 256; }
+
 bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   if (!a || a->B < 0 || a->M < 0 || a->M >= SVT_MAX_T || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0 ||
       (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16) || a->cap < 0 ||
@@ -1786,13 +1921,12 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   }
   if (!p->wide) p->nqb = (p->R + p->qb_rows - 1) / p->qb_rows;
   if (p->wide) {
-    // Partials: two slots of qb_rows rows per workgroup, plus the prefix of
-    // tiles per sequence.
+    // Partials: two slots of qb_rows rows per range, plus the prefix of
+    // tiles per sequence and one record per range.
     p->kc = 0;
     p->ns = 1;
     const size_t rows = (size_t)2 * p->grid * p->qb_rows;
-    const size_t pref_bytes = ((size_t)2 * (a->B + 1) * sizeof(int) + 255) / 256 * 256;
-    p->ws_bytes = pref_bytes + rows * (a->D * sizeof(_Float16) + sizeof(float4));
+    p->ws_bytes = stream_pref_bytes(a->B) + stream_meta_bytes(p->grid) + rows * (a->D * sizeof(_Float16) + sizeof(float4));
     return true;
   }
   // Prefix split size: enough workgroups to cover the chip several times over.
@@ -1825,17 +1959,19 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   d.seq_status = a->seq_status;
   if (p.wide) {
     unsigned char* w = static_cast<unsigned char*>(a->workspace);
-    const size_t pref_bytes = ((size_t)2 * (a->B + 1) * sizeof(int) + 255) / 256 * 256;
+    const size_t pref_bytes = stream_pref_bytes(a->B), meta_bytes = stream_meta_bytes(p.grid);
     const size_t rows = (size_t)2 * p.grid * p.qb_rows;
     d.ws_pref = reinterpret_cast<int*>(w);
-    d.ws_mls = reinterpret_cast<float4*>(w + pref_bytes);
-    d.ws_h = reinterpret_cast<_Float16*>(w + pref_bytes + rows * sizeof(float4));
+    d.ws_meta = reinterpret_cast<RangeMeta*>(w + pref_bytes);
+    d.ws_mls = reinterpret_cast<float4*>(w + pref_bytes + meta_bytes);
+    d.ws_h = reinterpret_cast<_Float16*>(w + pref_bytes + meta_bytes + rows * sizeof(float4));
     d.ws_o = nullptr;
     d.ws_ml = nullptr;
   } else {
     float* ws = static_cast<float*>(a->workspace);
     const size_t n_o = p.ns > 1 ? (size_t)a->B * a->Hkv * p.ns * p.R * a->D : 0;
     d.ws_pref = nullptr;
+    d.ws_meta = nullptr;
     d.ws_h = nullptr;
     d.ws_mls = nullptr;
     d.ws_o = ws;
@@ -1880,14 +2016,18 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
 #undef SVT_STREAM
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // One combine workgroup per (range, group of rows): the cut units are at
+    // most one per range; with a whole number of ranges per unit, one per
+    // (unit, group of rows).
     const int64_t nu = (int64_t)a->B * a->Hkv * p.nqb;
     if (nu > 0x7FFFFFF0) return hipErrorInvalidValue;
-    // dims per thread: the largest of 8, 4, 2 that still gives two workgroups per CU
+    const int64_t nwork = p.rpu > 0 ? nu : p.grid;
+    // dims per thread: the largest of 8, 4, 2 that still gives two working workgroups per CU
     const int want = 2 * p.grid;
-    const int dpt = (nu * ((p.qb_rows + 256 / (a->D / 8) - 1) / (256 / (a->D / 8))) >= want) ? 8
-                    : (nu * ((p.qb_rows + 256 / (a->D / 4) - 1) / (256 / (a->D / 4))) >= want) ? 4 : 2;
+    const int dpt = (nwork * ((p.qb_rows + 256 / (a->D / 8) - 1) / (256 / (a->D / 8))) >= want) ? 8
+                    : (nwork * ((p.qb_rows + 256 / (a->D / 4) - 1) / (256 / (a->D / 4))) >= want) ? 4 : 2;
     const int rpw = 256 / (a->D / dpt);
-    const dim3 cg((unsigned)nu, (unsigned)((p.qb_rows + rpw - 1) / rpw));
+    const dim3 cg((unsigned)(p.rpu > 0 ? nu : p.grid), (unsigned)((p.qb_rows + rpw - 1) / rpw));
 #define SVT_COMBINE(DD)                                                                                   \
   if (dpt == 8) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 8>), cg, dim3(256), 0, s, d);          \
   else if (dpt == 4) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 4>), cg, dim3(256), 0, s, d);     \
