@@ -2022,8 +2022,10 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     const int64_t nu = (int64_t)a->B * a->Hkv * p.nqb;
     if (nu > 0x7FFFFFF0) return hipErrorInvalidValue;
     const int64_t nwork = p.rpu > 0 ? nu : p.grid;
-    // dims per thread: the largest of 8, 4, 2 that still gives two working workgroups per CU
-    const int want = 2 * p.grid;
+    // dims per thread: the largest of 8, 4, 2 that still gives a working
+    // workgroup per CU (B=1 32K: 4 dims, 7.4 -> 5.6 us per combine against 2,
+    // which the rule asking two per CU gave)
+    const int want = p.grid;
     const int dpt = (nwork * ((p.qb_rows + 256 / (a->D / 8) - 1) / (256 / (a->D / 8))) >= want) ? 8
                     : (nwork * ((p.qb_rows + 256 / (a->D / 4) - 1) / (256 / (a->D / 4))) >= want) ? 4 : 2;
     const int rpw = 256 / (a->D / dpt);
