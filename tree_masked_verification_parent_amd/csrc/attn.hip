@@ -1740,10 +1740,9 @@ __global__ __launch_bounds__(256) void attn_fp32_kernel(AttnDev a) {
 // --------------------------------------------------------------------------
 // Split combine: one wave per query row, splits merged in index order.
 // --------------------------------------------------------------------------
-template <int D, typename E>
+template <int D, typename E, int KB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
   constexpr int DPL = D / 64;
-  constexpr int KB = 8;
   const int b = blockIdx.z, g = blockIdx.y;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -2063,13 +2062,17 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.ns <= 1) return e;
   const dim3 cgrid((p.R + 3) / 4, a->Hkv, a->B);
+  // the first batch of splits, loaded in one round trip with the lengths,
+  // covers every split when there are at most 16
+#define SVT_COMBINE_S(DD, EE)                                                                          \
+  if (p.ns <= 8) hipLaunchKernelGGL((attn_combine_kernel<DD, EE, 8>), cgrid, block, 0, s, d);         \
+  else hipLaunchKernelGGL((attn_combine_kernel<DD, EE, 16>), cgrid, block, 0, s, d);
   if (a->dtype == SVT_BF16) {
-    if (a->D == 128) hipLaunchKernelGGL((attn_combine_kernel<128, __bf16>), cgrid, block, 0, s, d);
-    else hipLaunchKernelGGL((attn_combine_kernel<64, __bf16>), cgrid, block, 0, s, d);
+    if (a->D == 128) { SVT_COMBINE_S(128, __bf16) } else { SVT_COMBINE_S(64, __bf16) }
   } else {
-    if (a->D == 128) hipLaunchKernelGGL((attn_combine_kernel<128, float>), cgrid, block, 0, s, d);
-    else hipLaunchKernelGGL((attn_combine_kernel<64, float>), cgrid, block, 0, s, d);
+    if (a->D == 128) { SVT_COMBINE_S(128, float) } else { SVT_COMBINE_S(64, float) }
   }
+#undef SVT_COMBINE_S
   return hipGetLastError();
 }
 
