@@ -17,6 +17,7 @@ dominant call, `roofline_attention` for the attention call.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -691,6 +692,12 @@ def main():
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(collectives and sharding are out of its scope); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    # Python's cyclic collector stays off for the whole run, as in timeit: a
+    # full collection over torch's object heap takes about 40 ms, and it would
+    # land inside whichever timed round or step crosses the threshold (one
+    # such pause tripled the B=8 EXSPEC verify total of the scheduling run).
+    gc.collect()
+    gc.disable()
     if args.sched:
         sched_bench(args)
         return
