@@ -170,14 +170,22 @@ typedef struct svt_attn_args {
   int32_t form;              /* svt_attn_form: which work decomposition (bf16 only)   */
   const int32_t* seq_slot;   /* [B] cache row of each sequence, or NULL (row b)        */
   int32_t n_slots;           /* rows of k_cache / v_cache when seq_slot is set         */
+  int32_t split_keys;        /* 0, or content keys per split (a positive multiple of  */
+                             /* 64): selects the split form with that split size, so */
+                             /* a sequence's result depends on its own inputs only   */
+                             /* (else SVT_ERR_ARG; with SVT_ATTN_STREAM too)          */
 } svt_attn_args;
 
 /* Work decomposition of svt_verify_attention (bf16; fp32 always splits).
  * Both compute the same function; results agree to rounding, and each is
  * bitwise reproducible for identical inputs.
  *   SVT_ATTN_AUTO    choose by shape
- *   SVT_ATTN_SPLIT   fixed key splits per (sequence, KV head); a sequence's
- *                    result does not depend on the rest of the batch
+ *   SVT_ATTN_SPLIT   key splits per (sequence, KV head), counted from the
+ *                    start of the sequence's content; their size comes from
+ *                    the shape (B, lmax_bound), or is fixed by split_keys,
+ *                    and then a sequence's result is bitwise the same in any
+ *                    batch ([BSD] section 4: batching must not change a
+ *                    sequence's output)
  *   SVT_ATTN_STREAM  the key tiles of the whole batch cut into one range of
  *                    equal cost per compute unit (needs bf16 and B <= 1024,
  *                    else SVT_ERR_UNSUPPORTED) */

@@ -207,7 +207,8 @@ def stream_units(B, T, Hq, Hkv, lens, cus, status=None):
     return units
 
 
-def run_attention(q, kc, vc, kt, vt, parents, lens, lmax_bound=None, status=None, scale=0.0, form=0, dev="cuda"):
+def run_attention(q, kc, vc, kt, vt, parents, lens, lmax_bound=None, status=None, scale=0.0, form=0, dev="cuda",
+                  split_keys=0):
     """svt_build_mask then svt_verify_attention on host arrays (bf16 as uint16
     bits).  The mask and tree status handed back for the comparison are the
     oracle's own, built from the parent arrays, after asserting that the GPU's
@@ -235,11 +236,11 @@ def run_attention(q, kc, vc, kt, vt, parents, lens, lmax_bound=None, status=None
     ln_t, lm_t = i32(lens), i32([lmax])
     bound = lmax if lmax_bound is None else lmax_bound
     args = svt.attn_args(tq, tkc, tvc, ln_t, lm_t, bound, tkt, tvt, mk, out, status=st, seq_status=sst,
-                         scale=scale, form=form)
+                         scale=scale, form=form, split_keys=split_keys)
     need = svt.svt_verify_attention_workspace(args)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     args = svt.attn_args(tq, tkc, tvc, ln_t, lm_t, bound, tkt, tvt, mk, out, status=st, seq_status=sst,
-                         scale=scale, workspace=ws, form=form)
+                         scale=scale, workspace=ws, form=form, split_keys=split_keys)
     rc = svt.svt_verify_attention(args)
     torch.cuda.synchronize()
     _, ost = oracle.validate(parents, M)

@@ -305,9 +305,9 @@ def _attn_case(w, lens, cap, seed, parents=None, poison=True):
     return q, kc, vc, kt, vt, parents, lens
 
 
-def _run_attn(w, q, kc, vc, kt, vt, parents, lens, lmax_bound=None, status=None, scale=0.0, form=0):
+def _run_attn(w, q, kc, vc, kt, vt, parents, lens, lmax_bound=None, status=None, scale=0.0, form=0, split_keys=0):
     return H.run_attention(q, kc, vc, kt, vt, parents, lens, lmax_bound=lmax_bound, status=status, scale=scale,
-                           form=form)
+                           form=form, split_keys=split_keys)
 
 
 def _small_w(base, **kw):
@@ -451,6 +451,56 @@ def test_attention_batch_equals_alone(form):
             alone = H.out_f32(w1, o1)[0]
             err = np.abs(alone - H.out_f32(w, out)[b]).max()
             assert err <= 1e-2 * np.abs(alone).max() + 1e-3, (b, err)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_attention_fixed_split_size_is_batch_invariant(dtype):
+    """With split_keys fixed, a sequence's output is bitwise the same in a
+    ragged batch (a grid sized for a larger bound, a skipped empty sequence
+    beside it) as computed alone: batching must not change a sequence's
+    output (Batch Speculative Decoding Done Right, ko summary, section 4).
+    The batch is also checked against the oracle.  Without split_keys a
+    batch of 40 sequences of 4000 keys gets 640-key splits and a lone such
+    sequence 256-key ones, so the fixed size is what makes the bits agree."""
+    w = _small_w(1, B=5, dtype=dtype, Hq=8, Hkv=2, D=128 if dtype == "bf16" else 64, M=16)
+    lens = np.array([2100, 1, 700, 0, 1333], np.int32)
+    q, kc, vc, kt, vt, par, lens = _attn_case(w, lens, 2300, 7400)
+    for sk in (64, 512):
+        rc, out, mk, ost, _ = _run_attn(w, q, kc, vc, kt, vt, par, lens, lmax_bound=2300, split_keys=sk)
+        assert rc == 0
+        full = H.from_dev(out)
+        _, ref = oracle.attention(wl.as_f32(w, q), wl.as_f32(w, kc), wl.as_f32(w, vc), wl.as_f32(w, kt),
+                                  wl.as_f32(w, vt), mk, lens, 2100, ost)
+        H.check_attention(w, H.out_f32(w, out), ref, f"split-keys-{sk}")
+        for b in range(len(lens)):
+            L = int(lens[b])
+            sl = slice(2100 - L, 2100) if L else slice(0, 1)  # an empty prefix: one unread column
+            w1 = _small_w(1, B=1, dtype=dtype, Hq=8, Hkv=2, D=w.D, M=16)
+            rc1, o1, _, _, _ = _run_attn(w1, q[b:b + 1], np.ascontiguousarray(kc[b:b + 1, :, sl]),
+                                         np.ascontiguousarray(vc[b:b + 1, :, sl]), kt[b:b + 1], vt[b:b + 1],
+                                         par[b:b + 1], lens[b:b + 1], split_keys=sk)
+            assert rc1 == 0 and np.array_equal(H.from_dev(o1)[0], full[b]), (sk, b)
+    # the property needs a fixed size: the shape-derived ones differ with the
+    # batch (split count from the partials' workspace, [B][Hkv][splits][R][D + 2] fp32)
+    def splits(B_):
+        a = svt.AttnArgs()
+        a.B, a.M, a.Hq, a.Hkv, a.D, a.dtype, a.cap, a.lmax_bound = B_, 16, 8, 2, 128, svt.SVT_BF16, 4000, 4000
+        a.form = svt.SVT_ATTN_SPLIT
+        return svt.svt_verify_attention_workspace(a) // (B_ * 2 * 68 * 130 * 4)
+    assert (splits(40), splits(1)) == (7, 16)
+
+
+def test_attention_split_keys_arguments():
+    """split_keys must be 0 or a positive multiple of 64, and selects the split
+    form: with SVT_ATTN_STREAM it is an argument error, found before any launch."""
+    w = _small_w(1, B=2, dtype="bf16", Hq=8, Hkv=2, D=128, M=8)
+    lens = np.array([300, 200], np.int32)
+    q, kc, vc, kt, vt, par, lens = _attn_case(w, lens, 320, 7500)
+    for sk, form in ((100, svt.SVT_ATTN_AUTO), (-64, svt.SVT_ATTN_SPLIT), (256, svt.SVT_ATTN_STREAM)):
+        rc, out, _, _, sst = _run_attn(w, q, kc, vc, kt, vt, par, lens, form=form, split_keys=sk)
+        assert rc == svt.SVT_ERR_ARG, (sk, form, rc)
+    rc, _, _, _, sst = _run_attn(w, q, kc, vc, kt, vt, par, lens, split_keys=256)  # AUTO: the split form
+    assert rc == 0 and (sst == 0).all()
 
 
 @pytest.mark.parametrize("form", FORMS[1:], ids=FORM_IDS[1:])

@@ -68,12 +68,14 @@ size_t svt_verify_attention_workspace(const svt_attn_args* a) {
 int svt_verify_attention(const svt_attn_args* a, hipStream_t stream) {
   char shape[160];
   if (!a) return finish("svt_verify_attention", SVT_ERR_ARG, "null args");
-  std::snprintf(shape, sizeof shape, "B=%d M=%d Hq=%d Hkv=%d D=%d dtype=%d cap=%lld lmax_bound=%d form=%d", a->B,
-                a->M, a->Hq, a->Hkv, a->D, a->dtype, (long long)a->cap, a->lmax_bound, a->form);
+  std::snprintf(shape, sizeof shape, "B=%d M=%d Hq=%d Hkv=%d D=%d dtype=%d cap=%lld lmax_bound=%d form=%d split_keys=%d",
+                a->B, a->M, a->Hq, a->Hkv, a->D, a->dtype, (long long)a->cap, a->lmax_bound, a->form, a->split_keys);
   if (a->B < 0 || a->M < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0 || a->cap < 0 ||
       a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap || !(a->scale >= 0.0f))
     return finish("svt_verify_attention", SVT_ERR_ARG, shape);
   if (a->form < SVT_ATTN_AUTO || a->form > SVT_ATTN_STREAM) return finish("svt_verify_attention", SVT_ERR_ARG, shape);
+  if (a->split_keys < 0 || a->split_keys % 64 != 0 || (a->split_keys > 0 && a->form == SVT_ATTN_STREAM))
+    return finish("svt_verify_attention", SVT_ERR_ARG, shape);
   if (a->seq_slot && a->n_slots <= 0) return finish("svt_verify_attention", SVT_ERR_ARG, shape);
   if (a->M >= SVT_MAX_T || (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16))
     return finish("svt_verify_attention", SVT_ERR_UNSUPPORTED, shape);

@@ -1752,7 +1752,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
   // sequence's lengths (their slots exist whatever the lengths are; slots of
   // splits the sequence does not use are loaded and ignored), so a call with
   // at most KB splits pays one memory round trip before the merge.  The
-  // arithmetic runs in split order: the maximum, then the weighted sums.
+  // arithmetic runs in split order: the maximum, then the weighted sums
+  // (fused multiply-adds, whatever the batch of loads).
   float mv[KB], lv[KB], ov[KB][DPL];
 #pragma unroll
   for (int j = 0; j < KB; ++j) {
@@ -1787,9 +1788,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
   for (int j = 0; j < KB; ++j) {
     if (j >= n0) break;
     const float w = exp2f(mv[j] - mu);
-    lsum += lv[j] * w;
+    lsum = fmaf(lv[j], w, lsum);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] += ov[j][e] * w;
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(ov[j][e], w, acc[e]);
   }
   for (int s0 = KB; s0 < ns_b; s0 += KB) {
 #pragma unroll
@@ -1804,9 +1805,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnDev a) {
     for (int j = 0; j < KB; ++j) {
       if (s0 + j >= ns_b) break;
       const float w = exp2f(mv[j] - mu);
-      lsum += lv[j] * w;
+      lsum = fmaf(lv[j], w, lsum);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += ov[j][e] * w;
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(ov[j][e], w, acc[e]);
     }
   }
   E* orow = static_cast<E*>(a.out) + (((int64_t)b * a.T + r % a.T) * a.Hq + g * a.G + r / a.T) * D;
@@ -1839,7 +1840,8 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   if (!a || a->B < 0 || a->M < 0 || a->M >= SVT_MAX_T || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0 ||
       (a->D != 64 && a->D != 128) || (a->dtype != SVT_FP32 && a->dtype != SVT_BF16) || a->cap < 0 ||
       a->form < SVT_ATTN_AUTO || a->form > SVT_ATTN_STREAM ||
-      a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap)
+      a->lmax_bound < 0 || (int64_t)a->lmax_bound > a->cap || a->split_keys < 0 || a->split_keys % KT != 0 ||
+      (a->split_keys > 0 && a->form == SVT_ATTN_STREAM))
     return false;
   p->T = a->M + 1;
   p->G = a->Hq / a->Hkv;
@@ -1854,7 +1856,7 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   const int cus = a->dtype == SVT_BF16 ? device_cu_count() : 0;
   const bool stream_ok = a->B <= kStreamMaxB;
   bool use_stream = stream_ok && stream_tiles >= 8 * (int64_t)cus;
-  if (a->form == SVT_ATTN_SPLIT) use_stream = false;
+  if (a->form == SVT_ATTN_SPLIT || a->split_keys > 0) use_stream = false;
   if (a->form == SVT_ATTN_STREAM) {
     if (a->dtype != SVT_BF16 || !stream_ok) return false;
     use_stream = true;
@@ -1934,6 +1936,9 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   const int64_t target = 1024;
   int64_t tiles_per_split = (units + target - 1) / target;
   if (tiles_per_split < 4) tiles_per_split = 4;
+  // a split size the caller fixes: the splits of a sequence no longer depend
+  // on the batch
+  if (a->split_keys > 0) tiles_per_split = a->split_keys / KT;
   p->kc = (int)(tiles_per_split * KT);
   p->ns = a->lmax_bound > 0 ? (int)((a->lmax_bound + p->kc - 1) / p->kc) : 1;
   if (p->ns < 1) p->ns = 1;

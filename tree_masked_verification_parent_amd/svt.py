@@ -47,7 +47,8 @@ class AttnArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("q", _P), ("k_cache", _P), ("v_cache", _P), ("cap", _I64),
                 ("len", _P), ("lmax", _P), ("lmax_bound", _I32), ("k_tree", _P), ("v_tree", _P), ("mask", _P),
                 ("status", _P), ("out", _P), ("seq_status", _P), ("workspace", _P),
-                ("workspace_bytes", ctypes.c_size_t), ("form", _I32), ("seq_slot", _P), ("n_slots", _I32)]
+                ("workspace_bytes", ctypes.c_size_t), ("form", _I32), ("seq_slot", _P), ("n_slots", _I32),
+                ("split_keys", _I32)]
 
 
 class AcceptArgs(ctypes.Structure):
@@ -174,7 +175,8 @@ def _dtype_code(t):
 
 
 def attn_args(q, k_cache, v_cache, lens, lmax, lmax_bound: int, k_tree, v_tree, mask, out, status=None,
-              seq_status=None, scale: float = 0.0, workspace=None, form: int = 0, seq_slot=None) -> AttnArgs:
+              seq_status=None, scale: float = 0.0, workspace=None, form: int = 0, seq_slot=None,
+              split_keys: int = 0) -> AttnArgs:
     B, T, Hq, D = q.shape
     a = AttnArgs()
     a.B, a.M, a.Hq, a.Hkv, a.D = B, T - 1, Hq, k_cache.shape[1], D
@@ -190,6 +192,7 @@ def attn_args(q, k_cache, v_cache, lens, lmax, lmax_bound: int, k_tree, v_tree, 
     a.form = int(form)
     a.seq_slot = _ptr(seq_slot)
     a.n_slots = k_cache.shape[0] if seq_slot is not None else 0
+    a.split_keys = int(split_keys)
     return _keep(a, q, k_cache, v_cache, lens, lmax, k_tree, v_tree, mask, out, status, seq_status, workspace, seq_slot)
 
 
