@@ -69,8 +69,15 @@ class RoundPipeline:
         acc = self._accept_args(self.sets[0])
         self.accept_ws = torch.empty(max(1, svt.svt_accept_workspace(acc)), dtype=torch.uint8, device=dev)
         self.attn_ws = torch.empty(1, dtype=torch.uint8, device=dev)
+        self._args = {}  # argument structs by (call, round parity[, layer]): built once, reused
 
     # ---- argument structs ---------------------------------------------------
+    def _cached(self, key, make):
+        a = self._args.get(key)
+        if a is None:
+            a = self._args[key] = make()
+        return a
+
     def _attn_args(self, s: _RoundSet, k: int, layer: int, ws=None):
         return svt.attn_args(s.q[layer], self.kv_main[layer, 0], self.kv_main[layer, 1], self.lens[k % 2],
                              self.lmax[k % 2], self.lmax_bound, s.kv_branch[layer, 0], s.kv_branch[layer, 1],
@@ -104,6 +111,7 @@ class RoundPipeline:
         need = svt.svt_verify_attention_workspace(self._attn_args(self.sets[0], 0, 0))
         if need > self.attn_ws.numel():
             self.attn_ws = torch.empty(need, dtype=torch.uint8, device=self.kv_main.device)
+        self._args = {}
 
     # ---- rounds -----------------------------------------------------------------
     def verify(self, k: int, stream=None) -> int:
@@ -111,12 +119,18 @@ class RoundPipeline:
         s = self.sets[k % 2]
         rc = svt.svt_build_mask(s.parents, self.M, s.mask, s.depth, s.status, 0, stream)
         for layer in range(self.L):
-            rc = rc or svt.svt_verify_attention(self._attn_args(s, k, layer, self.attn_ws), stream)
-        return rc or svt.svt_accept(self._accept_args(s), stream)
+            rc = rc or svt.svt_verify_attention(self._attn(s, k, layer), stream)
+        return rc or svt.svt_accept(self._cached(("accept", k % 2), lambda: self._accept_args(s)), stream)
+
+    def _attn(self, s, k, layer):
+        return self._cached(("attn", k % 2, layer), lambda: self._attn_args(s, k, layer, self.attn_ws))
+
+    def _commit(self, s, k, layer=None):
+        return self._cached(("commit", k % 2, layer), lambda: self._commit_args(s, k, layer))
 
     def commit(self, k: int, stream=None) -> int:
         """The whole commit of round k in one call."""
-        return svt.svt_commit(self._commit_args(self.sets[k % 2], k), 0, stream)
+        return svt.svt_commit(self._commit(self.sets[k % 2], k), 0, stream)
 
     def sequential_step(self, k: int) -> int:
         """Round k in order on the current stream: verify, then commit."""
@@ -131,18 +145,18 @@ class RoundPipeline:
         rc = 0
         if k > 0:
             prev = self.sets[(k - 1) % 2]
-            rc = svt.svt_commit(self._commit_args(prev, k - 1, -1), 0, main)
+            rc = svt.svt_commit(self._commit(prev, k - 1, -1), 0, main)
             self.side.wait_stream(main)
             for layer in range(self.L):
-                rc = rc or svt.svt_commit(self._commit_args(prev, k - 1, layer), 0, self.side)
+                rc = rc or svt.svt_commit(self._commit(prev, k - 1, layer), 0, self.side)
                 self._layer_done[layer].record(self.side)
         s = self.sets[k % 2]
         rc = rc or svt.svt_build_mask(s.parents, self.M, s.mask, s.depth, s.status, 0, main)
         for layer in range(self.L):
             if k > 0:
                 main.wait_event(self._layer_done[layer])
-            rc = rc or svt.svt_verify_attention(self._attn_args(s, k, layer, self.attn_ws), main)
-        rc = rc or svt.svt_accept(self._accept_args(s), main)
+            rc = rc or svt.svt_verify_attention(self._attn(s, k, layer), main)
+        rc = rc or svt.svt_accept(self._cached(("accept", k % 2), lambda: self._accept_args(s)), main)
         if k > 0:
             main.wait_stream(self.side)
         return rc
