@@ -15,8 +15,12 @@ from . import svt
 
 class VerifyRound:
     def __init__(self, B: int, M: int, Hq: int, Hkv: int, D: int, V: int, cap: int, n_layers: int,
-                 dtype: torch.dtype, device="cuda", attn_layers: int | None = None):
+                 dtype: torch.dtype, device="cuda", attn_layers: int | None = None, attn_split_keys: int = 0):
+        """attn_split_keys > 0 (a multiple of 64) runs attention in the split form
+        with splits of that many content keys, so that each sequence's output is
+        bitwise independent of the rest of the batch; 0 lets the library choose."""
         self.B, self.M, self.T, self.Hq, self.Hkv, self.D, self.V = B, M, M + 1, Hq, Hkv, D, V
+        self.attn_split_keys = int(attn_split_keys)
         self.cap, self.n_layers, self.dtype = cap, n_layers, dtype
         self.attn_layers = n_layers if attn_layers is None else attn_layers
         W = (self.T + 63) // 64
@@ -59,7 +63,7 @@ class VerifyRound:
         return svt.attn_args(self.q[layer], self.kv_main[layer, 0], self.kv_main[layer, 1], self.len, self.lmax,
                              self.lmax_bound, self.kv_branch[layer, 0], self.kv_branch[layer, 1], self.mask,
                              self.out[layer], status=self.status, seq_status=self.seq_status,
-                             workspace=self._attn_ws)
+                             workspace=self._attn_ws, split_keys=self.attn_split_keys)
 
     def _accept_args(self):
         return svt.accept_args(self.logits, self.tree_tokens, self.parents, self.mask, self.depth, self.amax,
