@@ -490,6 +490,30 @@ def test_attention_fixed_split_size_is_batch_invariant(dtype):
     assert (splits(40), splits(1)) == (7, 16)
 
 
+def test_verify_round_split_keys_matches_direct_call():
+    """VerifyRound(attn_split_keys=K) runs the same attention as a direct
+    svt_verify_attention call with split_keys=K: identical bits."""
+    from tree_masked_verification_parent_amd.round import VerifyRound
+    w = _small_w(1, B=3, dtype="bf16", Hq=8, Hkv=2, D=128, M=16)
+    cap = 1000
+    q, kc, vc, kt, vt, par, lens = _attn_case(w, np.array([900, 17, 400], np.int32), cap, 7600)
+    rc, ref, _, _, _ = _run_attn(w, q, kc, vc, kt, vt, par, lens, lmax_bound=cap, split_keys=512)
+    assert rc == 0
+    r = VerifyRound(w.B, w.M, w.Hq, w.Hkv, w.D, 64, cap, 1, torch.bfloat16, attn_split_keys=512)
+    r.q[0].copy_(H.to_dev(q))
+    r.kv_main[0, 0].copy_(H.to_dev(kc))
+    r.kv_main[0, 1].copy_(H.to_dev(vc))
+    r.kv_branch[0, 0].copy_(H.to_dev(kt))
+    r.kv_branch[0, 1].copy_(H.to_dev(vt))
+    r.parents.copy_(torch.from_numpy(par))
+    r.len.copy_(torch.from_numpy(lens))
+    r.lmax.fill_(int(lens.max()))
+    r.set_lmax_bound(cap)
+    assert r.build_mask() == 0 and r.attention(0) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(H.from_dev(r.out[0]), H.from_dev(ref))
+
+
 def test_attention_split_keys_arguments():
     """split_keys must be 0 or a positive multiple of 64, and selects the split
     form: with SVT_ATTN_STREAM it is an argument error, found before any launch."""
