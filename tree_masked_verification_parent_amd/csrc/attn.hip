@@ -1379,7 +1379,7 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
 // one memory round trip.  A
 // unit spread over more ranges lists the rest of its pieces (empty ranges
 // skipped) in LDS, one range per lane, and merges them in batches of
-// KB = 32 / DPT pieces.  With a whole number of ranges per unit (one
+// KB = 32 / DPT pieces (4 at 16 dims).  With a whole number of ranges per unit (one
 // sequence) the pieces are known without the record: see below.
 constexpr int kMaxPieces = 64;  // pieces listed per pass (one wave)
 
@@ -1387,7 +1387,7 @@ template <int D, int DPT>
 __global__ __launch_bounds__(256) void attn_stream_combine_kernel(AttnDev a) {
   constexpr int TPR = D / DPT;   // threads per row
   constexpr int RPW = 256 / TPR; // rows per workgroup
-  constexpr int KB = 32 / DPT;  // pieces loaded per batch
+  constexpr int KB = DPT >= 16 ? 4 : 32 / DPT;  // pieces loaded per batch
   typedef _Float16 f16xN __attribute__((ext_vector_type(DPT)));
   int cr = blockIdx.x;  // range (with a whole number of ranges per unit: the unit)
   const int G = a.stream_grid;
@@ -2026,16 +2026,18 @@ hipError_t launch_attention(const svt_attn_args* a, const AttnPlan& p, hipStream
     const int64_t nu = (int64_t)a->B * a->Hkv * p.nqb;
     if (nu > 0x7FFFFFF0) return hipErrorInvalidValue;
     const int64_t nwork = p.rpu > 0 ? nu : p.grid;
-    // dims per thread: the largest of 8, 4, 2 that still gives a working
+    // dims per thread: the largest of 16, 8, 4, 2 that still gives a working
     // workgroup per CU (B=1 32K: 4 dims, 7.4 -> 5.6 us per combine against 2,
-    // which the rule asking two per CU gave)
+    // which the rule asking two per CU gave; B=8 and B=32: 16 dims, 0.8 and
+    // about 1 us per call less than 8; 32 dims were slower at both)
     const int want = p.grid;
-    const int dpt = (nwork * ((p.qb_rows + 256 / (a->D / 8) - 1) / (256 / (a->D / 8))) >= want) ? 8
-                    : (nwork * ((p.qb_rows + 256 / (a->D / 4) - 1) / (256 / (a->D / 4))) >= want) ? 4 : 2;
+    auto groups = [&](int k) { return nwork * ((p.qb_rows + 256 / (a->D / k) - 1) / (256 / (a->D / k))); };
+    const int dpt = groups(16) >= want ? 16 : groups(8) >= want ? 8 : groups(4) >= want ? 4 : 2;
     const int rpw = 256 / (a->D / dpt);
     const dim3 cg((unsigned)(p.rpu > 0 ? nu : p.grid), (unsigned)((p.qb_rows + rpw - 1) / rpw));
 #define SVT_COMBINE(DD)                                                                                   \
-  if (dpt == 8) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 8>), cg, dim3(256), 0, s, d);          \
+  if (dpt == 16) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 16>), cg, dim3(256), 0, s, d);        \
+  else if (dpt == 8) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 8>), cg, dim3(256), 0, s, d);     \
   else if (dpt == 4) hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 4>), cg, dim3(256), 0, s, d);     \
   else hipLaunchKernelGGL((attn_stream_combine_kernel<DD, 2>), cg, dim3(256), 0, s, d);
     if (a->D == 128) { SVT_COMBINE(128) } else { SVT_COMBINE(64) }
