@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--pipeline", action="store_true",
                     help="round time of the B=32 workload with the commit of each round overlapped layer by layer "
                          "with the next round's attention (eager and HIP graph) against sequential rounds")
+    ap.add_argument("--attn-sweep", action="store_true",
+                    help="attention alone over batch sizes and prefix-length ranges (GQA 32/8, D=128, M=32, "
+                         "bf16, inputs cycled so that none is cached), in the automatic, split and stream forms")
     ap.add_argument("--eager", action="store_true",
                     help="time steps launched call by call from the host (per-call events then include any time "
                          "the GPU waits for the next launch) instead of replays of one HIP graph of the step")
@@ -122,7 +125,7 @@ MALL_BYTES = 256 << 20  # MI355X Infinity Cache
 
 
 def cold_attention(torch, svt, r, len0, lmax0_t, attn_bytes, attn_flops, total=1 << 30, max_copies=256,
-                   eager=False):
+                   eager=False, form=0):
     """Attention timed over copies of one layer's inputs (Q, prefix and tree
     K/V, output) totalling at least `total` bytes of attention reads, cycled
     so that no call finds its inputs in the Infinity Cache.  The round above
@@ -139,7 +142,7 @@ def cold_attention(torch, svt, r, len0, lmax0_t, attn_bytes, attn_flops, total=1
         out = torch.empty_like(r.out[0])
         keep.append((q, kv, br, out))
         args.append(svt.attn_args(q, kv[0], kv[1], r.len, r.lmax, r.lmax_bound, br[0], br[1], r.mask, out,
-                                  status=r.status, seq_status=r.seq_status, workspace=r._attn_ws))
+                                  status=r.status, seq_status=r.seq_status, workspace=r._attn_ws, form=form))
     for a in args:  # one untimed pass
         assert svt.svt_verify_attention(a) == 0
     passes = max(1, -(-64 // n))
@@ -517,6 +520,72 @@ def sweep_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def attn_sweep_bench(args):
+    """svt_verify_attention alone over batch sizes and prefix-length ranges on
+    the B=32 workload's head shapes (GQA 32/8, D=128, M=32, bf16): per call,
+    HIP events over copies of the inputs cycled so that none is read from the
+    Infinity Cache (as bench.py's cold attention), in the automatic choice and
+    in each form forced.  Prints one JSON line."""
+    import dataclasses
+
+    import torch
+    from synth import workloads as wl
+    from tree_masked_verification_parent_amd import svt
+    from tree_masked_verification_parent_amd.round import VerifyRound
+
+    base = wl.workload(4)
+    dev = torch.device("cuda")
+    grid = [((1024, 8192), (1, 2, 4, 8, 16, 32, 64)), ((128, 1024), (32, 64, 128, 256, 512))]
+    forms = [("auto", svt.SVT_ATTN_AUTO), ("split", svt.SVT_ATTN_SPLIT), ("stream", svt.SVT_ATTN_STREAM)]
+    rows = []
+    for (lo, hi), bs in grid:
+        for B in bs:
+            w = dataclasses.replace(base, B=B, len_lo=lo, len_hi=hi)
+            lens0 = wl.lengths(w)
+            lmax0 = int(lens0.max())
+            r = VerifyRound(B, w.M, w.Hq, w.Hkv, w.D, 64, lmax0 + w.T + 64, 1, torch.bfloat16, attn_layers=1)
+            gen_t = torch.Generator(device=dev)
+            gen_t.manual_seed(w.seed + B)
+            r.kv_main.normal_(0.0, w.qkv_sigma, generator=gen_t)
+            r.kv_branch.normal_(0.0, w.qkv_sigma, generator=gen_t)
+            r.q.normal_(0.0, w.qkv_sigma, generator=gen_t)
+            r.parents.copy_(torch.from_numpy(wl.trees(w)))
+            len0 = torch.from_numpy(lens0).to(dev)
+            lmax0_t = torch.tensor([lmax0], dtype=torch.int32, device=dev)
+            r.len.copy_(len0)
+            r.lmax.copy_(lmax0_t)
+            assert r.build_mask() == 0
+            nbytes = algorithmic_bytes_attention(w, lens0, w.T)
+            res = {"B": B, "len_range": [lo, hi], "sum_len": int(lens0.sum()), "attn_bytes": nbytes}
+            r.set_lmax_bound(lmax0)
+            # one discarded measurement first: the clock ramps up after the set-up
+            cold_attention(torch, svt, r, len0, lmax0_t, nbytes, 0.0)
+            for name, form in forms:
+                a = r._attn_args(0)
+                a.form = form
+                need = svt.svt_verify_attention_workspace(a)
+                if need == 0 and form == svt.SVT_ATTN_STREAM:
+                    res[name] = None   # the stream form does not take this batch
+                    continue
+                if need > (0 if r._attn_ws is None else r._attn_ws.numel()):
+                    r._attn_ws = torch.empty(need, dtype=torch.uint8, device=dev)
+                c = cold_attention(torch, svt, r, len0, lmax0_t, nbytes, 0.0, form=form)
+                res[name] = {"us_per_call": c["us_per_call"], "GBps": c["GBps"], "frac_hbm": c["frac_hbm"]}
+            rows.append(res)
+            best = min((v["us_per_call"], k) for k, v in res.items() if isinstance(v, dict))
+            print(f"[attn-sweep] B={B:4d} len U[{lo},{hi}]: " + ", ".join(
+                f"{k} {v['us_per_call']:.1f} us ({v['frac_hbm']:.0%})" for k, v in res.items() if isinstance(v, dict))
+                + f"; fastest {best[1]}", file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
+    out = {"metric": "attention alone: us per call and fraction of 8 TB/s, cold, by batch size and prefix length",
+           "unit": "us per call", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+           "data": "synthetic (seeded trees and lengths; device-seeded normal Q/K/V)",
+           "config": {"workload": "B=32 workload head shapes (GQA 32/8, D=128, M=32), B and lengths varied"},
+           "results": rows}
+    print(json.dumps(out), flush=True)
+
+
 def interop_bench(args):
     """svt_expand_mask (three output kinds) and svt_commit_length against
     svt_commit on the B=32 workload (M=32, prefix U[1024, 8192], 36 layers).
@@ -709,6 +778,9 @@ def main():
         return
     if args.pipeline:
         pipeline_bench(args)
+        return
+    if args.attn_sweep:
+        attn_sweep_bench(args)
         return
 
     import torch
