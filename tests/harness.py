@@ -121,13 +121,16 @@ class StreamUnit:
     cuts: list         # stream tiles inside (base, base + ntl) where a range starts
 
 
-def stream_plan(B, T, Hq, Hkv, cus):
+def stream_plan(B, T, Hq, Hkv, cus, lmax_bound=0, D=128):
     """(nqb, qb_rows, compute waves, set-up charge) of the stream form: at
-    most 12 query tiles per unit, 8 when the batch has fewer units than CUs;
-    the units of a KV head split its tiles as evenly as whole tiles allow."""
+    most 12 query tiles per unit, 8 when the batch has fewer units than CUs
+    and its K/V bound (B Hkv lmax_bound rows of K and V, bf16) is at most
+    192 MiB; the units of a KV head split its tiles as evenly as whole tiles
+    allow."""
     R = (Hq // Hkv) * T
     nqt = (R + 15) // 16
-    cap = 8 if B * Hkv * ((nqt + 11) // 12) < cus else 12
+    few = B * Hkv * ((nqt + 11) // 12) < cus and B * Hkv * lmax_bound * D * 4 <= (192 << 20)
+    cap = 8 if few else 12
     nqb = (nqt + cap - 1) // cap
     tpb = (nqt + nqb - 1) // nqb
     nw = tpb if tpb <= 2 else 4 if tpb <= 4 else 6 if tpb <= 6 else 8 if tpb <= 8 else 9 if tpb <= 9 else 12
@@ -140,25 +143,27 @@ def unit_rows(nqt, nqb, qb, R):
     return 16 * ((qb * nqt) // nqb), min(R, 16 * (((qb + 1) * nqt) // nqb))
 
 
-def stream_grid(B, T, Hq, Hkv, cus):
+def stream_grid(B, T, Hq, Hkv, cus, lmax_bound=0, D=128):
     """Ranges of the stream form: one per CU, or for a single sequence the
     largest whole number of ranges per unit that leaves at most a tenth of
     the CUs idle."""
-    nqb, _, _, _ = stream_plan(B, T, Hq, Hkv, cus)
+    nqb, _, _, _ = stream_plan(B, T, Hq, Hkv, cus, lmax_bound, D)
     units = Hkv * nqb
     if B == 1 and units <= cus and 10 * units * (cus // units) >= 9 * cus:
         return units * (cus // units)
     return cus
 
 
-def stream_units(B, T, Hq, Hkv, lens, cus, status=None):
+def stream_units(B, T, Hq, Hkv, lens, cus, status=None, lmax_bound=None, D=128):
     """Units of the stream form in stream order, each with the range starts
     that fall strictly inside it (a unit with cuts is merged from partials),
-    for a device of `cus` compute units."""
+    for a device of `cus` compute units (lmax_bound: the call's host bound,
+    by default the longest length)."""
     G = Hq // Hkv
     R = G * T
-    grid = stream_grid(B, T, Hq, Hkv, cus)
-    nqb, qb_rows, nw, pc = stream_plan(B, T, Hq, Hkv, cus)
+    bound = (int(np.max(lens)) if len(lens) else 0) if lmax_bound is None else int(lmax_bound)
+    grid = stream_grid(B, T, Hq, Hkv, cus, bound, D)
+    nqb, qb_rows, nw, pc = stream_plan(B, T, Hq, Hkv, cus, bound, D)
     nqt = (R + 15) // 16
     ntree = (T + KT - 1) // KT
     tiles = []

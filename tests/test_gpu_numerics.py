@@ -111,7 +111,7 @@ def test_attention_planted_large_scores(form, shape):
     q, kc, vc, kt, vt = _inputs(w, lens, lmax + 16, 9301, w.qkv_sigma, w.qkv_sigma)
     _, ost = oracle.validate(par, w.M)
     omk, _ = oracle.mask(par, w.M, ost)
-    units = H.stream_units(w.B, w.T, w.Hq, w.Hkv, lens, H.cu_count())
+    units = H.stream_units(w.B, w.T, w.Hq, w.Hkv, lens, H.cu_count(), D=w.D)
     rng = np.random.default_rng(9302)
     lam = 400.0
     slots = {}     # (b, g, "cache" | "tree", position) -> (i, h, where); a later plant replaces an earlier one

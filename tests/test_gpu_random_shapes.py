@@ -79,3 +79,28 @@ def test_attention_random_shape(name, over, lens, extra, sigma, seed):
                                         to_f32=lambda x: wl.as_f32(w, x))
         sel = np.stack([got[b, i, h] for b, i, h in rows])
         H.check_attention(w, sel, ref, f"{name} form {form}")
+
+
+def test_attention_few_units_large_kv():
+    """Fewer units than CUs with K/V beyond the bound where units of 8 query
+    tiles pay off (here 268 MB of K and V): the stream form keeps units of up
+    to 12 tiles, each spread over many ranges; two nodes of every (sequence,
+    query head) against the oracle, in every form."""
+    w = dataclasses.replace(wl.workload(1), B=4, dtype="bf16", Hq=32, Hkv=8, D=128, M=32)
+    lens = np.array([16384, 12000, 9000, 3000], np.int32)
+    assert 4 * 8 * 16384 * 128 * 4 > (192 << 20)
+    nqb, _, nw, _ = H.stream_plan(w.B, w.T, w.Hq, w.Hkv, H.cu_count(), 16384, w.D)
+    assert (nqb, nw) == (1, 9)
+    q, kc, vc, kt, vt = wl.attention_inputs(w, lens, 16384 + 16, 2100)
+    par = wl.trees(w, 2100)
+    rng = np.random.default_rng(2101)
+    rows = [(b, int(i), h) for b in range(w.B) for h in range(w.Hq) for i in rng.choice(w.T, 2, replace=False)]
+    ref = None
+    for form in (svt.SVT_ATTN_AUTO, svt.SVT_ATTN_SPLIT, svt.SVT_ATTN_STREAM):
+        print(f"[few-units-large-kv] form {form}", flush=True)
+        rc, out, omk, ost, sst = H.run_attention(q, kc, vc, kt, vt, par, lens, form=form)
+        assert rc == 0 and (sst == 0).all()
+        got = H.out_f32(w, out)
+        if ref is None:
+            ref = oracle.attention_rows(q, kc, vc, kt, vt, omk, lens, 16384, rows, to_f32=lambda x: wl.as_f32(w, x))
+        H.check_attention(w, np.stack([got[b, i, h] for b, i, h in rows]), ref, f"form {form}")

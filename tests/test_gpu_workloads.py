@@ -102,7 +102,7 @@ def test_workload_attention(wi):
     # units that range ends cut, which go through the partial merge
     rows = [(b, i, h) for b in range(w.B) for i in range(w.T) for h in range(w.Hq)]
     if w.dtype == "bf16" and w.B <= 1024:
-        units = H.stream_units(w.B, w.T, w.Hq, w.Hkv, lens, H.cu_count())
+        units = H.stream_units(w.B, w.T, w.Hq, w.Hkv, lens, H.cu_count(), D=w.D)
         print(f"[{w.name}] {sum(1 for u in units if u.cuts)} of {len(units)} stream units are cut", flush=True)
     print(f"[{w.name}] oracle on all {len(rows)} rows, {oracle.default_threads()} threads", flush=True)
     ref = oracle.attention_rows(q, kc, vc, kt, vt, omk, lens, lmax, rows, to_f32=lambda x: wl.as_f32(w, x))

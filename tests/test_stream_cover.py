@@ -36,14 +36,14 @@ def _paths(over, lens):
         found.add("lds-search")
     if lens is None:
         return found
-    nqb, _, _, pc = H.stream_plan(B, T, Hq, Hkv, CUS)
+    nqb, _, _, pc = H.stream_plan(B, T, Hq, Hkv, CUS, int(lens.max()), over["D"])
     units = Hkv * nqb
     if B == 1 and units <= CUS and 10 * units * (CUS // units) >= 9 * CUS:
         rpu = CUS // units
         ntl = (int(lens[0]) + H.KT - 1) // H.KT + (T + H.KT - 1) // H.KT
         found.add("whole-ranges" if (ntl + pc) // rpu >= pc + 2 else "whole-ranges-fallback")
         return found
-    for u in H.stream_units(B, T, Hq, Hkv, lens, CUS):
+    for u in H.stream_units(B, T, Hq, Hkv, lens, CUS, D=over["D"]):
         if len(u.cuts) == 1:
             found.add("cut-once")
         elif len(u.cuts) >= 2:

@@ -1880,14 +1880,20 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
     // Stream form: up to 12 query tiles per unit, spread evenly over the
     // fewest units per KV head, one tile per compute wave (plus the two
     // producer waves); one workgroup per CU.  With fewer units than CUs
-    // (one long sequence: every unit is cut into many pieces and the key
-    // tiles stream from L2) units of at most 8 tiles are faster: B=1 32K
-    // 56.6 -> 53.8 us per call against 12.
+    // units of at most 8 tiles are faster (B=1 32K 56.6 -> 53.8 us per call,
+    // B=2 of up to 8192 keys 37.3 -> 27.7 us) as long as the K/V they read
+    // twice stays in the 256 MB Infinity Cache; with more K/V the second
+    // query block's reads go to HBM and 12 are faster (B=8 of up to 8192
+    // keys 62.8 -> 52.2 us, B=16 106.1 -> 80.3 us, B=4 of up to 16384 keys
+    // 64.9 -> 56.7 us).  The K/V bound is the host's: B Hkv lmax_bound rows
+    // of K and V.
 #ifndef SVT_STREAM_FEW_TPB
 #define SVT_STREAM_FEW_TPB 8
 #endif
     int cap_t = 12;
-    if ((int64_t)a->B * a->Hkv * ((p->nqt + 11) / 12) < (int64_t)cus) cap_t = SVT_STREAM_FEW_TPB;
+    const int64_t kv_bound = (int64_t)a->B * a->Hkv * a->lmax_bound * a->D * 4;
+    if ((int64_t)a->B * a->Hkv * ((p->nqt + 11) / 12) < (int64_t)cus && kv_bound <= (int64_t)192 << 20)
+      cap_t = SVT_STREAM_FEW_TPB;
     const int nqb = (p->nqt + cap_t - 1) / cap_t;
     const int tpb = (p->nqt + nqb - 1) / nqb;
     p->wide = 1;
