@@ -1855,12 +1855,14 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
                                (((int64_t)a->lmax_bound + KT - 1) / KT + (p->T + KT - 1) / KT);
   const int cus = a->dtype == SVT_BF16 ? device_cu_count() : 0;
   const bool stream_ok = a->B <= kStreamMaxB;
-  // The stream form from two key tiles per CU on (GQA 32/8, D=128, M=32, equal
-  // lengths, split against stream: at one tile per CU the split form is faster
-  // by up to 30 %, at two they are within 10 % of each other, from four on the
-  // stream form is 15-40 % faster, e.g. B=16 of 512 keys 35.2 -> 20.7 us and B=1 of
-  // 8192 keys 34.8 -> 25.1 us).
-  bool use_stream = stream_ok && stream_tiles >= 2 * (int64_t)cus;
+  // The stream form from two D=128 key tiles' worth of bytes per CU on (GQA
+  // 32/8, D=128, M=32, equal lengths, split against stream: at one tile per CU
+  // the split form is faster by up to 30 %, at two they are within 10 % of
+  // each other, from four on the stream form is 15-40 % faster, e.g. B=16 of
+  // 512 keys 35.2 -> 20.7 us and B=1 of 8192 keys 34.8 -> 25.1 us; at D=64,
+  // whose tiles hold half the bytes, B=4 of up to 2048 keys, about two tiles
+  // per CU: split 15.4 us, stream 19.1 us).
+  bool use_stream = stream_ok && stream_tiles * a->D >= 2 * 128 * (int64_t)cus;
   if (a->form == SVT_ATTN_SPLIT || a->split_keys > 0) use_stream = false;
   if (a->form == SVT_ATTN_STREAM) {
     if (a->dtype != SVT_BF16 || !stream_ok) return false;
