@@ -1863,6 +1863,14 @@ bool plan_attention(const svt_attn_args* a, AttnPlan* p) {
   // whose tiles hold half the bytes, B=4 of up to 2048 keys, about two tiles
   // per CU: split 15.4 us, stream 19.1 us).
   bool use_stream = stream_ok && stream_tiles * a->D >= 2 * 128 * (int64_t)cus;
+  // At most 64 query rows per KV head (MHA, say), so that the split form too
+  // reads each key once, and at least four (sequence, KV head) pairs per CU:
+  // the split form, which skips the stream form's per-unit set-up and merge
+  // (MHA 32/32, M=16: B=128 of up to 256 keys 116.6 -> 105.0 us, at D=64
+  // 81.0 -> 54.4 us; B=64 of up to 1024 keys 171.1 -> 163.0 us; MHA 16/16, M=32:
+  // B=64 of up to 1024 keys 96.9 -> 90.2 us; within 2 % either way at B=32 of up
+  // to 4096 keys, and 10-20 % slower below four pairs per CU).
+  if (p->R <= 64 && (int64_t)a->B * a->Hkv >= 4 * (int64_t)cus) use_stream = false;
   if (a->form == SVT_ATTN_SPLIT || a->split_keys > 0) use_stream = false;
   if (a->form == SVT_ATTN_STREAM) {
     if (a->dtype != SVT_BF16 || !stream_ok) return false;
