@@ -385,10 +385,13 @@ MANY_CASES = [
     # prefix scan runs in several passes), one query tile per KV head
     ("b300-decode-1wave", dict(B=300, dtype="bf16", Hq=2, Hkv=2, D=64, M=0), 150),
     ("b1024-M3-1wave", dict(B=1024, dtype="bf16", Hq=1, Hkv=1, D=64, M=3), 80),
+    # MHA with at most 64 query rows per KV head and four (sequence, KV head)
+    # pairs per CU: the automatic choice takes the split form
+    ("b64-mha16-M16", dict(B=64, dtype="bf16", Hq=16, Hkv=16, D=128, M=16), 300),
 ]
 
 
-@pytest.mark.parametrize("form", FORMS[1:], ids=FORM_IDS[1:])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("name,over,lmax", MANY_CASES, ids=[c[0] for c in MANY_CASES])
 def test_attention_many_sequences(name, over, lmax, form):
     w = _small_w(1, **over)
