@@ -723,11 +723,10 @@ def pipeline_bench(args):
     t_pip = run(p.pipelined_step, k, R)
     k += R
     p.attn_form = svt.SVT_ATTN_SPLIT         # the split form schedules many small workgroups
-    p.set_lmax_bound(cap)
+    p.set_lmax_bound(cap)                    # its workspace differs
     t_pip_split = run(p.pipelined_step, k, R)
     k += R
     p.attn_form = svt.SVT_ATTN_AUTO
-    p.set_lmax_bound(cap)
     graphs = {0: p.capture(k + (k % 2)), 1: p.capture(k + 1 - (k % 2))}
 
     def replay(kk):

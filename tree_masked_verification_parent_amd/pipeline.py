@@ -50,7 +50,8 @@ class RoundPipeline:
     def __init__(self, B: int, M: int, Hq: int, Hkv: int, D: int, V: int, cap: int, n_layers: int,
                  dtype: torch.dtype, device="cuda", attn_form: int = svt.SVT_ATTN_AUTO):
         dev = torch.device(device)
-        self.attn_form = attn_form
+        self._args = {}
+        self._attn_form = attn_form
         self.B, self.M, self.T, self.L, self.cap = B, M, M + 1, n_layers, cap
         i32 = dict(dtype=torch.int32, device=dev)
         self.kv_main = torch.zeros(n_layers, 2, B, Hkv, cap, D, dtype=dtype, device=dev)
@@ -72,6 +73,15 @@ class RoundPipeline:
         self._args = {}  # argument structs by (call, round parity[, layer]): built once, reused
 
     # ---- argument structs ---------------------------------------------------
+    @property
+    def attn_form(self) -> int:
+        return self._attn_form
+
+    @attn_form.setter
+    def attn_form(self, form: int):
+        self._attn_form = form
+        self._args = {}  # the cached attention structs carry the form
+
     def _cached(self, key, make):
         a = self._args.get(key)
         if a is None:
