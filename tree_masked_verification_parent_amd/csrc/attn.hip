@@ -1047,13 +1047,14 @@ __global__ __launch_bounds__((NW + 2) * 64) void attn_bf16_stream_kernel(AttnDev
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
     voff[dt] = vrow * TL::ROWB + 16 * ((2 * dt + (q4 >> 1)) ^ TL::swz_v(vrow)) + 8 * (q4 & 1);
-  // With at most eight compute waves the tile loop is unrolled over the four
-  // ring stages, so that each stage's LDS offsets sit in the read
-  // instructions; stages 2 and 3 lie beyond their 16-bit offset field and
-  // read from these copies of the lane offsets moved up by two stages
-  // (B=1 32K: 24 fewer VALU instructions per tile, 1-2 % faster, bitwise the
-  // same; with nine waves, whose registers are short, it was 2 % slower).
-  constexpr bool kStaticStages = NW * QMAX <= 8;
+  // With eight compute waves (two per SIMD, bound by the SIMDs' issue) the
+  // tile loop is unrolled over the four ring stages, so that each stage's LDS
+  // offsets sit in the read instructions; stages 2 and 3 lie beyond their
+  // 16-bit offset field and read from these copies of the lane offsets moved
+  // up by two stages (B=1 32K: 24 fewer VALU instructions per tile, 1-3 %
+  // faster, bitwise the same; with nine waves, whose registers are short, 2 %
+  // slower, and with two, bound by memory, no faster).
+  constexpr bool kStaticStages = NW * QMAX == 8;
   int koff_hi[kStaticStages ? NKS : 1], voff_hi[kStaticStages ? NDT : 1];
   if constexpr (kStaticStages) {
 #pragma unroll
